@@ -1,0 +1,22 @@
+"""CPU oracle for fused attention forward.
+
+TEST INFRASTRUCTURE ONLY.  Imported by ``tests/``, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py``; never by the product package.  It
+shares no code with the HIP path.
+
+* ``attention_ref`` -- float64 two-pass softmax attention (the definition).
+* ``online_attention_ref`` -- float64 online-softmax recurrence over any key
+  tiling, used to pin the recurrence against the definition.
+
+Pins (all in ``tests/test_oracle.py``): the worked two-tile example of the
+page "22. GPU Engineering: Correctness, Throughput, and Attention" (sec. 22.7),
+closed forms (one key, zero scale, causal first row), invariants (rows of P sum
+to one, constant V, score shift, key/query permutation), an independent
+library routine (torch's float64 scaled-dot-product attention), a 50-digit
+brute force on tiny inputs, and the recurrence under every tiling.
+"""
+from .attention_ref import attention_ref, attention_ref_batched, bf16_bits_to_f64, f32_scale
+from .online_ref import all_compositions, online_attention_ref, uniform_bounds
+
+__all__ = ["attention_ref", "attention_ref_batched", "bf16_bits_to_f64", "f32_scale",
+           "online_attention_ref", "all_compositions", "uniform_bounds"]
