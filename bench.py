@@ -1,0 +1,176 @@
+"""Benchmark: fused attention forward TFLOP/s on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline]
+                    [--no-cpu-baseline]
+
+A step is one attention forward over the whole workload (B=2, H=32, N=8192,
+d=128, causal, Q and K scaled by 4 -- the headline case) with inputs already
+resident in HBM.  W untimed warm-up steps, then K timed steps bracketed by
+device synchronisation; the kernel's own average duration is taken with HIP
+events recorded on the launch stream around the same K launches.  Flops are
+the algorithmic count 4*B*H*N^2*d, halved when causal (page "GPU Programming &
+Kernel Development", Self-check: fusion does not change the flop count).
+
+Prints ONE JSON line.  ``cpu_baseline`` times the float64 oracle (as it is) on
+a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s + % of bf16 MFMA peak (N=8192, d=128, causal)"
+PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+
+
+def cpu_baseline(w, budget_s: float = 15.0, rows_per_head: int = 2048):
+    """Time the float64 oracle on a seeded row sample of every head, head by
+    head, until the time budget is spent.  Returns the JSON object."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention_ref, bf16_bits_to_f64, f32_scale
+    from tiled_attention_09_amd.synth import bf16_bits, make_workload, sample_rows
+
+    q, k, v = make_workload(w)
+    s = f32_scale(w.scale)
+    flops = 0.0
+    heads = 0
+    t0 = time.perf_counter()
+    for b in range(w.B):
+        for h in range(w.H):
+            rows = sample_rows(w.N, rows_per_head, w.seed + 100 + b * w.H + h)
+            qd = bf16_bits_to_f64(bf16_bits(q[b, h]))
+            kd = bf16_bits_to_f64(bf16_bits(k[b, h]))
+            vd = bf16_bits_to_f64(bf16_bits(v[b, h]))
+            attention_ref(qd, kd, vd, s, w.causal, rows=rows)
+            visible = (rows + 1) if w.causal else np.full(rows.size, w.N)
+            flops += float(4 * w.d * visible.sum())
+            heads += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        else:
+            continue
+        break
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": "float64 two-pass oracle on %d heads x %d seeded query rows "
+                      "(all N keys, causal mask), %.1f s; value = algorithmic flops of "
+                      "those rows / wall time; host cores visible %d" % (
+                          heads, min(rows_per_head, w.N), dt, len(os.sched_getaffinity(0)))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="headline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: heads shard across GPUs with no exchange, "
+              "so there is no multi-GPU path to time (got --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import tiled_attention_09_amd as ta
+    from tiled_attention_09_amd.synth import WORKLOADS, make_workload
+
+    w = WORKLOADS[args.workload]
+    ta.load_library()
+    dev = torch.device("cuda:0")
+    q, k, v = (x.to(dev) for x in make_workload(w))
+    o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ta.attn_fwd(q, k, v, w.scale, w.causal, out=o, lse=lse, stream=stream.cuda_stream)
+
+    torch.cuda.synchronize()
+    t_cold = time.perf_counter()
+    step()
+    torch.cuda.synchronize()
+    cold_ms = (time.perf_counter() - t_cold) * 1e3
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ms_per_step = wall_ms / args.steps
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+
+    # per-launch spread (median / p10 / p90) from individually bracketed launches
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(min(args.steps, 30))]
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in evs)
+    med = per[len(per) // 2]
+
+    tflops = w.flops / (ms_per_step * 1e-3) / 1e12
+    achieved = w.flops / (kernel_ms * 1e-3) / 1e12
+    prof_traffic = os.path.join(ROOT, "profiles", "traffic_%s.json" % w.name)
+    traffic = None
+    if os.path.exists(prof_traffic):
+        traffic = json.load(open(prof_traffic)).get("bytes_per_launch")
+
+    props = torch.cuda.get_device_properties(dev)
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "attention fwd " + w.describe(), "B": w.B, "H": w.H, "N": w.N,
+                   "d": w.d, "causal": w.causal, "seed": w.seed, "out_dtype": "fp32"},
+        "pct_of_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "kernel_ms": {"mean": round(kernel_ms, 5), "median": round(med, 5),
+                      "p10": round(per[len(per) // 10], 5), "p90": round(per[(9 * len(per)) // 10], 5),
+                      "cold_first_call_ms": round(cold_ms, 3)},
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                   "cus": props.multi_processor_count, "hip": torch.version.hip},
+        "flops_per_step": w.flops,
+        "alg_bytes_per_step": w.alg_bytes,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,78 @@
+/*
+ * tiledattn.h -- C ABI of the fused attention-forward library for AMD
+ * Instinct MI355X (gfx950).  Library file: libtiledattn.so.
+ *
+ * The operation is softmax attention with an online (tiled) softmax: for
+ * every (batch, head) and query row i,
+ *
+ *     S[i,j] = scale * <q_i, k_j>          (hidden when causal and j > i)
+ *     O[i,:] = sum_j softmax_j(S[i,:]) v_j
+ *     LSE[i] = ln sum_j exp(S[i,j])        (natural log, scaled scores)
+ *
+ * computed tile by tile with a running maximum, normaliser and unnormalised
+ * accumulator, so the N x N score matrix is never stored.  Definitions:
+ * page "22. GPU Engineering: Correctness, Throughput, and Attention",
+ * sec. 22.5 (the recurrence, masking before max and sum) and sec. 22.7 (the
+ * causal rule on absolute positions and the saved per-row log-normaliser);
+ * page "GPU Programming & Kernel Development" (FlashAttention: tiles streamed
+ * on chip, the score matrix never written).
+ *
+ * Nothing here depends on HIP headers; a stream is passed as an opaque
+ * pointer (a hipStream_t; NULL selects the default stream).
+ */
+#ifndef TILEDATTN_H
+#define TILEDATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+typedef enum {
+  TA_OK = 0,              /* enqueued (or nothing to do)                          */
+  TA_ERR_INVALID_ARG = 1, /* a size, flag, pointer or scale is out of range       */
+  TA_ERR_UNSUPPORTED = 2, /* head dimension other than 64 or 128                  */
+  TA_ERR_MISALIGNED = 3,  /* q, k, v or o not 16-byte aligned, lse not 4-byte     */
+  TA_ERR_HIP = 4          /* the HIP runtime reported an error at launch          */
+} ta_status;
+
+/*
+ * attn_fwd -- enqueue one fused attention forward on `stream`.
+ *
+ *   q, k, v : device pointers, bfloat16, contiguous row-major [B, H, N, d]
+ *             (the head's rows are consecutive, d fastest).  Read only.
+ *   o       : device pointer, float32, [B, H, N, d], written.
+ *   lse     : device pointer, float32, [B, H, N], written: natural-log
+ *             log-sum-exp of the scaled (and masked) scores of each row.
+ *   B, H, N : batch, heads, sequence length (queries = keys = N); each >= 1,
+ *             N <= 2^22 and B*H*ceil(N/128) <= 2^31-1.
+ *   d       : head dimension, 64 or 128.
+ *   scale   : multiplies Q K^T before the softmax; any finite float (callers
+ *             usually pass 1/sqrt(d)).
+ *   causal  : 0 = every key visible; 1 = key j visible to query i iff j <= i.
+ *   stream  : hipStream_t to enqueue on (NULL = default stream).
+ *
+ * Ownership: the caller allocates and frees every buffer; the library keeps no
+ * state and allocates nothing, so concurrent calls on different streams are
+ * safe.  o and lse must not overlap q, k or v.
+ *
+ * Synchronisation: the call only enqueues; results are valid once `stream`
+ * has been synchronised.  Q, K and V are expected to be finite (not checked
+ * on the device: a non-finite input makes the affected rows non-finite).
+ *
+ * Errors: argument errors are found before any HIP call, nothing is enqueued
+ * and the matching TA_ERR_* code is returned.  A launch rejected by the
+ * runtime returns TA_ERR_HIP (hipGetLastError is consumed).  Device faults
+ * surface at the caller's next synchronisation, as for any HIP kernel.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
+             int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/* Human-readable text for a ta_status value (static storage; never NULL). */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TILEDATTN_H */

@@ -1,0 +1,109 @@
+"""CPU tests of the C-ABI library: it loads, exports what the header declares,
+and rejects bad arguments before any HIP call (so no GPU is needed)."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import tiled_attention_09_amd as ta
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tiledattn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ta.library_path()),
+                                reason="libtiledattn.so not built (run __graft_entry__.build())")
+
+
+def _gpu_visible() -> bool:
+    import torch
+    return torch.cuda.device_count() > 0   # counts devices without initialising HIP
+
+
+# The fake-address tests are host-logic tests: never run them where a GPU could
+# execute a launch that slipped through a validation bug.
+host_only = pytest.mark.skipif(_gpu_visible(), reason="fake-address checks run on hosts without a GPU")
+
+# Fake, suitably aligned addresses: every call below must be rejected by the
+# argument checks, so these are never dereferenced and no kernel is enqueued.
+A = 0x100000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_entry_points():
+    assert declared_functions() == ["attn_fwd", "attn_status_string"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ta.load_library()
+    out = subprocess.run(["nm", "-D", "--defined-only", ta.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings():
+    for st in range(5):
+        assert ta.attn_status_string(st)
+    assert ta.attn_status_string(99) == "unknown status"
+    assert "head dimension" in ta.attn_status_string(ta.TA_ERR_UNSUPPORTED)
+
+
+def call(**over):
+    args = dict(q=A, k=A, v=A, o=A, lse=A, B=1, H=1, N=128, d=64, scale=0.125, causal=0)
+    args.update(over)
+    return ta.attn_fwd_raw(args["q"], args["k"], args["v"], args["o"], args["lse"], args["B"],
+                           args["H"], args["N"], args["d"], args["scale"], args["causal"], 0)
+
+
+@host_only
+@pytest.mark.parametrize("field", ["q", "k", "v", "o", "lse"])
+def test_null_pointer(field):
+    assert call(**{field: 0}) == ta.TA_ERR_INVALID_ARG
+
+
+@host_only
+@pytest.mark.parametrize("over", [dict(B=0), dict(H=0), dict(N=0), dict(B=-1), dict(N=(1 << 22) + 1),
+                                  dict(causal=2), dict(causal=-1), dict(scale=math.inf),
+                                  dict(scale=-math.inf), dict(scale=math.nan),
+                                  dict(B=1 << 16, H=1 << 15, N=1 << 20)])
+def test_invalid_sizes_flags_scale(over):
+    assert call(**over) == ta.TA_ERR_INVALID_ARG
+
+
+@host_only
+@pytest.mark.parametrize("d", [0, 16, 32, 96, 100, 256])
+def test_unsupported_head_dim(d):
+    assert call(d=d) == ta.TA_ERR_UNSUPPORTED
+
+
+@host_only
+@pytest.mark.parametrize("field,val", [("q", A + 8), ("k", A + 2), ("v", A + 4), ("o", A + 8),
+                                       ("lse", A + 2), ("lse", A + 1)])
+def test_misaligned(field, val):
+    # every other argument valid and d supported: the call must stop at the alignment check
+    assert call(**{field: val}) == ta.TA_ERR_MISALIGNED
+
+
+def test_python_wrapper_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ta.attn_fwd(x, x, x)
+
+
+def test_ctypes_signature():
+    lib = ta.load_library()
+    assert lib.attn_fwd.restype is ctypes.c_int
+    assert len(lib.attn_fwd.argtypes) == 12

@@ -1,0 +1,55 @@
+"""Build libtiledattn.so in-tree with hipcc for gfx950.
+
+    python -m tiled_attention_09_amd.build        # or __graft_entry__.build()
+
+Always recompiles.  The kernel resource report (VGPR/AGPR/SGPR, LDS, spills,
+occupancy) from ``-Rpass-analysis=kernel-resource-usage`` is written to
+``_build/resource_usage.txt`` (not committed).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SRC = os.path.join(HERE, "csrc", "attn_fwd.hip")
+INCLUDE = os.path.join(ROOT, "include")
+OUT = os.path.join(HERE, "libtiledattn.so")
+BUILD_DIR = os.path.join(ROOT, "_build")
+
+# Packed fp32 VALU forms are kept off: the compiler would otherwise fuse
+# pairs of fp32 multiplies into them.
+HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-Rpass-analysis=kernel-resource-usage"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def build_library(extra_flags=(), verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    tmp = OUT + ".tmp"
+    cmd = [hipcc()] + HIPCC_FLAGS + list(extra_flags) + ["-I", INCLUDE, SRC, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    report = os.path.join(BUILD_DIR, "resource_usage.txt")
+    with open(report, "w") as f:
+        f.write(" ".join(cmd) + "\n" + res.stdout + res.stderr)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed (%d); see %s" % (res.returncode, report))
+    os.replace(tmp, OUT)
+    if verbose:
+        print("built", OUT)
+    return OUT
+
+
+if __name__ == "__main__":
+    build_library(sys.argv[1:], verbose=True)
