@@ -21,9 +21,17 @@ int launch(const void* q, const void* k, const void* v, float* o, float* lse, in
            int n_qt, float scale_log2, hipStream_t stream) {
   const dim3 grid((unsigned)(bh * n_qt));
   const dim3 block(tiledattn::kThreads);
-  tiledattn::attn_fwd_kernel<D, CAUSAL><<<grid, block, 0, stream>>>(
-      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-      static_cast<const uint16_t*>(v), o, lse, bh, N, n_qt, scale_log2);
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kk = static_cast<const uint16_t*>(k);
+  const uint16_t* vv = static_cast<const uint16_t*>(v);
+  // A positive scale lets the row maximum be taken on raw scores (one fused
+  // multiply-add per exponent); zero or negative scales take the scaled path.
+  if (scale_log2 > 0.f)
+    tiledattn::attn_fwd_kernel<D, CAUSAL, true><<<grid, block, 0, stream>>>(
+        qq, kk, vv, o, lse, bh, N, n_qt, scale_log2);
+  else
+    tiledattn::attn_fwd_kernel<D, CAUSAL, false><<<grid, block, 0, stream>>>(
+        qq, kk, vv, o, lse, bh, N, n_qt, scale_log2);
   return hipGetLastError() == hipSuccess ? TA_OK : TA_ERR_HIP;
 }
 

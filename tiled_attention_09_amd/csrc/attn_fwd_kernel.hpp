@@ -1,40 +1,44 @@
 // Fused attention forward for gfx950 (MI355X): one workgroup owns a tile of
 // BM query rows of one (batch, head) and streams that head's keys and values
-// through LDS in tiles of BN, keeping the online-softmax state in registers.
+// through LDS in tiles of BN keys, keeping the online-softmax state in
+// registers, so the score matrix never reaches HBM.
 //
 // Method (page "22. GPU Engineering: Correctness, Throughput, and Attention",
 // sec. 22.5): per query row a running maximum m, normaliser l and
 // unnormalised accumulator o start at -inf, 0, 0; each score tile S updates
 //   m' = max(m, max S),  alpha = exp(m - m'),  p = exp(S - m'),
 //   l' = alpha l + sum p,  o' = alpha o + p V_tile,
-// and the output is o / l.  Hidden (future or non-existent) keys are set to
-// -inf before the maximum and the sum.  A row whose maximum is still -inf uses
-// 0 as exponent reference (sec. 22.7 lab).  The per-row log-normaliser
-// m + ln l is stored beside O (sec. 22.7: the statistic a recomputing backward
-// needs).  Exponentials are taken base 2 with log2(e) folded into the score
-// scale; the stored LSE is converted back to natural log.
+// and the output is o / l.  Hidden (future or non-existent) keys get -inf
+// before the maximum and the sum.  A row whose maximum is still -inf uses 0 as
+// exponent reference (sec. 22.7 lab).  The per-row log-normaliser m + ln l is
+// stored beside O (sec. 22.7: the statistic a recomputing backward needs).
+// Exponentials are taken base 2 with log2(e) folded into the score scale; the
+// stored LSE is converted back to natural log.
 //
-// Mapping to CDNA4 (wave64, MFMA 32x32x16 bf16 with fp32 accumulation):
-//  * Each of the 4 waves owns 32 query rows.  Scores are computed transposed,
-//    S^T = K Q^T, so an MFMA accumulator gives each lane one query (lane%32)
-//    and 16 keys of it; the row max/sum is then 15 in-lane ops plus one
-//    exchange between the two wave halves (instead of a 32-lane reduction).
-//  * The same accumulator, rounded to bf16, is directly the B operand of
-//    O^T = V^T P^T; O^T accumulates in fp32 registers for the whole loop, and
-//    its lane%32 column is again the lane's own query, so the alpha rescale is
-//    lane-local.
-//  * K is staged row-major in LDS, rows padded by 16 bytes (conflict-free
-//    128-bit reads of 16 consecutive rows).  V is staged transposed (V^T,
-//    keys contiguous) with a key permutation inside each group of 16 keys so
-//    that the 8 keys a wave half needs for one MFMA are contiguous.
-//  * Global tiles are read with 128-bit buffer loads whose range check
-//    returns zeros past the end of the head (ragged N: zero K rows are then
-//    masked, zero V rows keep 0 * garbage out of the sum).  The next tile's
-//    loads are issued before the current tile's math (register double
-//    buffering), so HBM/L2 latency hides under MFMA work.
-//  * Causal: a query tile only visits key tiles up to its last row; a wave
-//    whose rows are all before a key tile skips that tile's math; element
-//    masks are applied only on tiles that straddle the diagonal or the end.
+// Mapping to CDNA4 (wave64; MFMA 32x32x16 bf16, fp32 accumulation):
+//  * 4 waves x 32 query rows.  Scores are computed transposed, S^T = K Q^T,
+//    so an accumulator gives each lane one query (lane % 32) and 16 of its
+//    keys: the row max/sum is in-lane work plus one exchange between the two
+//    wave halves.  Q stays in VGPRs as the B operand for the whole loop.
+//  * The same accumulator, rounded to bf16, is the B operand of
+//    O^T = V^T P^T; O^T accumulates in fp32 registers and its column is again
+//    the lane's own query, so the alpha rescale is lane-local.
+//  * K and V tiles are copied HBM/L2 -> LDS by the buffer unit itself
+//    (buffer_load ... lds, 16 bytes per lane, no VGPR staging), two stages
+//    deep: tile j+1 is in flight while tile j is multiplied; one barrier per
+//    tile.  The buffer range check returns zeros past the end of the head, so
+//    a ragged last tile needs no guard (zero V rows also keep 0 * garbage out
+//    of the sum).
+//  * Both tiles keep the row-major [key][d] layout with the 16-byte chunks of
+//    each row XOR-swizzled by the row index.  K is read row-wise as the MFMA A
+//    operand (16 consecutive rows per 16 lanes hit 16 different chunk slots);
+//    V is read with the LDS transpose read (ds_read_b64_tr_b16): each 16-lane
+//    group receives a 16(d) x 4(keys) block transposed, which is exactly the
+//    V^T operand, and the 4 key rows of a half-wave land in 4 different 64-byte
+//    bank groups.
+//  * Causal: a query tile visits key tiles only up to its last row; a wave
+//    whose rows all precede a key tile skips its math; element masks are
+//    applied only on tiles that cross the diagonal or the end of the sequence.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -45,8 +49,8 @@ namespace tiledattn {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kWaves = 4;
@@ -56,17 +60,27 @@ constexpr int kBN = 64;           // keys per LDS tile
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
 constexpr float kLn2 = 0.69314718055994530942f;
 
+#define TA_LDS __attribute__((address_space(3)))
+
 template <int D>
 struct Tile {
   static_assert(D == 64 || D == 128, "head dim");
   static constexpr int KS = D / 16;                 // MFMA k-steps over d for S^T
   static constexpr int DB = D / 32;                 // 32-row blocks of O^T
-  static constexpr int KSTR = D + 8;                // bf16 per K row in LDS
-  static constexpr int VSTR = kBN + 8;              // bf16 per V^T row in LDS
-  static constexpr int CHUNKS = kBN * D / 8;        // 16-byte chunks per tile
-  static constexpr int CPT = CHUNKS / kThreads;     // chunks per thread (4 or 2)
-  static constexpr int DCH = D / 8;                 // 16-byte chunks per row
-  static_assert(CPT * kThreads == CHUNKS, "tile split");
+  static constexpr int DCH = D / 8;                 // 16-byte chunks per key row
+  static constexpr int BYTES = kBN * D * 2;         // one K or V tile
+  static constexpr int LOADS = BYTES / (kThreads * 16);   // 16-byte loads per thread per tile
+  static_assert(LOADS * kThreads * 16 == BYTES, "tile split");
+
+  // XOR applied to the chunk index of key row r.  d=128 (16 chunks): bijective
+  // on any 16 aligned rows, and rows 4a..4a+3 get 4 different 64-byte groups.
+  // d=64 (8 chunks, two rows per 256-byte bank window): bijective on the rows
+  // of one parity within 16 rows, and rows 4a, 4a+2 (and 4a+1, 4a+3) get
+  // different 64-byte groups.
+  __device__ static __forceinline__ int swz(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  }
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -75,14 +89,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
-}
-
-// Position of key r (0..15) inside its 16-key group of the V^T tile: bits 2
-// and 3 exchanged, so keys {0-3, 8-11} fill slots 0-7 and {4-7, 12-15} slots
-// 8-15 -- the two halves of a wave each read 8 contiguous slots.
-__device__ __forceinline__ int vpos(int key) {
-  const int r = key & 15;
-  return (key & ~15) | (r & 3) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
 // Workgroup -> (head, query tile).  Workgroups are handed to the 8 XCDs
@@ -99,18 +105,38 @@ __device__ __forceinline__ void map_block(int bid, int bh_count, int n_qt, bool 
   qt = causal ? n_qt - 1 - t : t;
 }
 
-template <int D, bool CAUSAL>
+// Enqueue the copy of key tile j (K and V) into one LDS stage.  Load i of
+// wave w fills bytes [(4 i + w) * 1024, +1024) of the stage's tile, one 16-byte
+// chunk per lane; src_off holds each lane's offset within a tile.
+template <int D>
+__device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                           const uint32_t* src_off, int j, int wave,
+                                           TA_LDS uint16_t* kd, TA_LDS uint16_t* vd) {
+  const uint32_t tile_off = (uint32_t)j * (uint32_t)Tile<D>::BYTES;   // scalar
+#pragma unroll
+  for (int i = 0; i < Tile<D>::LOADS; ++i) {
+    const int dst = (4 * i + wave) * 512;   // uint16 elements, wave-uniform
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (TA_LDS void*)(kd + dst), 16, src_off[i],
+                                             tile_off, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (TA_LDS void*)(vd + dst), 16, src_off[i],
+                                             tile_off, 0, 0);
+  }
+}
+
+template <int D, bool CAUSAL, bool POS_SCALE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, float* __restrict__ O,
                      float* __restrict__ LSE, int bh_count, int N, int n_qt, float scale_log2) {
   using T = Tile<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kBN * T::KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[D * T::VSTR];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[kBN * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
@@ -132,136 +158,151 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   for (int ks = 0; ks < T::KS; ++ks)
     qf[ks] = __builtin_bit_cast(bf16x8, load16(qr, (uint32_t)(my_q * D + 16 * ks + 8 * hi) * 2u));
 
+  // Tile copy offsets: LDS chunk p = (4 i + w) * 64 + lane holds key row
+  // p / DCH, global chunk (p % DCH) ^ swz(row).  They are the same for every
+  // tile and for K and V.
+  uint32_t src_off[T::LOADS];
+#pragma unroll
+  for (int i = 0; i < T::LOADS; ++i) {
+    const int p = (4 * i + wave) * 64 + lane;
+    const int row = p / T::DCH;
+    const int chunk = (p % T::DCH) ^ T::swz(row);
+    src_off[i] = (uint32_t)(row * D + chunk * 8) * 2u;
+  }
+  // Per-lane LDS byte offsets of the operand reads (tile-relative).
+  // K (A operand of S^T): row kb*32 + l32, chunk (2 ks + hi) ^ swz(l32).
+  const int kswz = T::swz(l32);
+  // V (A operand of O^T via transpose read): for read r of key group g and
+  // d block db, source lane reads 4 d-values at key 16 g + 8 r + 4 hi + (lane%16)/4,
+  // d = 32 db + 16 ((lane >> 4) & 1) + 4 (lane & 3).
+  const int vkey_lo = 4 * hi + ((lane & 15) >> 2);                 // key within an 8-key slice
+  const int vd_lo = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);       // d within a 32-d block
+
   f32x16 oacc[T::DB];
 #pragma unroll
   for (int db = 0; db < T::DB; ++db)
+#pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  float m = -__builtin_inff();   // running max of log2-domain scores (whole row)
-  float l = 0.f;                 // running normaliser (this wave half's keys)
+  // Running max: raw-score domain when the scale is positive (max commutes
+  // with the scale), scaled log2 domain otherwise.
+  float m = -__builtin_inff();
+  float l = 0.f;               // running normaliser (this wave half's keys)
 
   const int n_kt_all = (N + kBN - 1) / kBN;
   const int n_kt = CAUSAL ? min(n_kt_all, (qt + 1) * (kBM / kBN)) : n_kt_all;
 
-  // Staging assignment.  K: chunk c = tid + 256 i -> key c / DCH, chunk c % DCH.
-  // V: this thread owns CPT consecutive keys at one 8-wide d chunk.
-  const int v_dc = tid % T::DCH;
-  const int v_k0 = (tid / T::DCH) * T::CPT;
-
-  u32x4 kreg[T::CPT], vreg[T::CPT];
-  auto load_tile = [&](int j) {
+  auto compute_tile = [&](int j, const TA_LDS uint16_t* kt, const TA_LDS uint16_t* vt) {
     const int key0 = j * kBN;
-#pragma unroll
-    for (int i = 0; i < T::CPT; ++i) {
-      const int c = tid + kThreads * i;
-      const int key = key0 + c / T::DCH;
-      kreg[i] = load16(kr, (uint32_t)(key * D + (c % T::DCH) * 8) * 2u);
-    }
-#pragma unroll
-    for (int i = 0; i < T::CPT; ++i)
-      vreg[i] = load16(vr, (uint32_t)((key0 + v_k0 + i) * D + v_dc * 8) * 2u);
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < T::CPT; ++i) {
-      const int c = tid + kThreads * i;
-      *reinterpret_cast<u32x4*>(&k_lds[(c / T::DCH) * T::KSTR + (c % T::DCH) * 8]) = kreg[i];
-    }
-    // Transpose V: d row (8 v_dc + e) receives this thread's CPT keys.
-    const int col = vpos(v_k0);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      if constexpr (T::CPT == 4) {
-        const u32x2 ev = {(vreg[0][w] & 0xffffu) | (vreg[1][w] << 16),
-                          (vreg[2][w] & 0xffffu) | (vreg[3][w] << 16)};
-        const u32x2 od = {(vreg[0][w] >> 16) | (vreg[1][w] & 0xffff0000u),
-                          (vreg[2][w] >> 16) | (vreg[3][w] & 0xffff0000u)};
-        *reinterpret_cast<u32x2*>(&v_lds[(v_dc * 8 + 2 * w) * T::VSTR + col]) = ev;
-        *reinterpret_cast<u32x2*>(&v_lds[(v_dc * 8 + 2 * w + 1) * T::VSTR + col]) = od;
-      } else {
-        const uint32_t ev = (vreg[0][w] & 0xffffu) | (vreg[1][w] << 16);
-        const uint32_t od = (vreg[0][w] >> 16) | (vreg[1][w] & 0xffff0000u);
-        *reinterpret_cast<uint32_t*>(&v_lds[(v_dc * 8 + 2 * w) * T::VSTR + col]) = ev;
-        *reinterpret_cast<uint32_t*>(&v_lds[(v_dc * 8 + 2 * w + 1) * T::VSTR + col]) = od;
-      }
-    }
-  };
-
-  load_tile(0);
-  for (int j = 0; j < n_kt; ++j) {
-    __syncthreads();                 // all waves are done reading tile j-1
-    store_tile();
-    __syncthreads();                 // tile j is visible in LDS
-    if (j + 1 < n_kt) load_tile(j + 1);
-
-    const int key0 = j * kBN;
-    if (CAUSAL && key0 > q0 + 31) continue;   // every key of this tile is in this wave's future
-
     // S^T (64 keys x 32 queries): block kb covers keys key0 + 32 kb + [0, 32).
     f32x16 s[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < T::KS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            &k_lds[(kb * 32 + l32) * T::KSTR + 16 * ks + 8 * hi]);
+    for (int ks = 0; ks < T::KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int row = kb * 32 + l32;
+        const bf16x8 a = *reinterpret_cast<const TA_LDS bf16x8*>(
+            kt + row * D + (((2 * ks + hi) ^ kswz) << 3));
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
       }
+
+    // Hide future / non-existent keys (only tiles crossing the diagonal or the end).
+    const bool edge = (CAUSAL && key0 + kBN - 1 > q0) || (key0 + kBN > N);
+    if (!POS_SCALE) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] *= scale_log2;
+    }
+    if (edge) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
+          if ((CAUSAL && key > my_q) || key >= N) s[kb][i] = -__builtin_inff();
+        }
     }
 
-    // Scale into the log2 domain; hide future / non-existent keys.
-    const bool edge = (CAUSAL && key0 + kBN - 1 > q0) || (key0 + kBN > N);
+    // Row maximum: 32 in-lane values (a chain of 3-input maxima), then the
+    // other wave half.
+    float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float t = s[kb][i] * scale_log2;
-        if (edge) {
-          const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-          if ((CAUSAL && key > my_q) || key >= N) t = -__builtin_inff();
-        }
-        s[kb][i] = t;
-      }
-
-    // Row maximum: 32 in-lane values, then the other wave half.
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    for (int i = 2; i < 32; i += 2)
+      mx = fmaxf(fmaxf(mx, s[i >> 4][i & 15]), s[(i + 1) >> 4][(i + 1) & 15]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
 
+    // m' = max(m, max S) and alpha = exp(m - m') (in log2 units); the safe
+    // reference keeps a row with no visible key yet away from -inf - -inf.
     const float m_new = fmaxf(m, mx);
-    const float ref = (m_new == -__builtin_inff()) ? 0.f : m_new;   // safe reference
-    const float alpha = __builtin_amdgcn_exp2f(m - ref);
+    const float ref = (m_new == -__builtin_inff()) ? 0.f : m_new;
+    const float cref = POS_SCALE ? ref * scale_log2 : ref;
+    const float alpha = __builtin_amdgcn_exp2f((POS_SCALE ? m * scale_log2 : m) - cref);
     m = m_new;
+    // Rescale l and o only when some row of this wave moved its maximum.
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    }
 
+    // p = 2^(c s - c m'); positive scale: one fused multiply-add per element.
+    // The row maximum itself gets p = 1 exactly, so the dominant weight carries
+    // no bf16 rounding into the value product.
     float psum = 0.f;
-    bf16x8 pf[2][2];
+    bf16x8 pf[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(s[kb][i] - ref);
+        const float arg = POS_SCALE ? __builtin_fmaf(s[kb][i], scale_log2, -cref) : s[kb][i] - cref;
+        const float p = __builtin_amdgcn_exp2f(arg);
         psum += p;
-        pf[kb][i >> 3][i & 7] = (__bf16)p;
+        pf[kb * 2 + (i >> 3)][i & 7] = (__bf16)p;
       }
-    l = alpha * l + psum;
-
-#pragma unroll
-    for (int db = 0; db < T::DB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    l += psum;
 
     // O^T (d x 32 queries) += V^T (d x 64 keys) P^T (64 keys x 32 queries).
 #pragma unroll
-    for (int db = 0; db < T::DB; ++db)
+    for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            &v_lds[(db * 32 + l32) * T::VSTR + g * 16 + 8 * hi]);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[g >> 1][g & 1], oacc[db], 0, 0, 0);
+      for (int db = 0; db < T::DB; ++db) {
+        s16x4 part[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int key = 16 * g + 8 * r + vkey_lo;
+          const int d = 32 * db + vd_lo;
+          const int off = key * D + ((((d >> 3) ^ T::swz(key)) << 3) | (d & 7));
+          part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (TA_LDS s16x4*)(vt + off));
+        }
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[g], oacc[db], 0, 0, 0);
       }
+  };
+
+  // Two-stage pipeline, unrolled by two so each stage's buffers are static.
+  TA_LDS uint16_t* const k0 = (TA_LDS uint16_t*)k_lds0;
+  TA_LDS uint16_t* const v0 = (TA_LDS uint16_t*)v_lds0;
+  TA_LDS uint16_t* const k1 = (TA_LDS uint16_t*)k_lds1;
+  TA_LDS uint16_t* const v1 = (TA_LDS uint16_t*)v_lds1;
+  issue_tile<D>(kr, vr, src_off, 0, wave, k0, v0);
+  for (int j = 0; j < n_kt; j += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();                       // tile j visible; tile j-1's readers done
+    if (j + 1 < n_kt) issue_tile<D>(kr, vr, src_off, j + 1, wave, k1, v1);
+    if (!(CAUSAL && j * kBN > q0 + 31)) compute_tile(j, k0, v0);
+    if (j + 1 >= n_kt) break;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (j + 2 < n_kt) issue_tile<D>(kr, vr, src_off, j + 2, wave, k0, v0);
+    if (!(CAUSAL && (j + 1) * kBN > q0 + 31)) compute_tile(j + 1, k1, v1);
   }
 
   // Epilogue: combine the two halves' normalisers, O = o / l, LSE = m + log2 l (as ln).
@@ -277,7 +318,8 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                      oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv};
         *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * g + 4 * hi) = val;
       }
-    if (hi == 0) LSE[(size_t)bh * N + my_q] = (m + __log2f(l_row)) * kLn2;
+    const float mlog2 = POS_SCALE ? m * scale_log2 : m;
+    if (hi == 0) LSE[(size_t)bh * N + my_q] = (mlog2 + __log2f(l_row)) * kLn2;
   }
 }
 
