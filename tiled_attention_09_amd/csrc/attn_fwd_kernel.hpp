@@ -91,6 +91,16 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
+// Both halves of a wave hold partial results for the same 32 queries; the
+// swap (v_permlane32_swap) gives every lane the other half's value without a
+// trip through LDS.
+__device__ __forceinline__ float other_half(float x) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false,
+                                                   false);
+  // lanes 0-31: pr[1] holds lanes 32-63; lanes 32-63: pr[0] holds lanes 0-31
+  return __int_as_float((threadIdx.x & 32) ? pr[0] : pr[1]);
+}
+
 // Workgroup -> (head, query tile).  Workgroups are handed to the 8 XCDs
 // round-robin, so block b runs on XCD b % 8; consecutive logical indices are
 // given to the same XCD so one head's query tiles share that XCD's L2.
@@ -194,7 +204,11 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   auto compute_tile = [&](int j, const TA_LDS uint16_t* kt, const TA_LDS uint16_t* vt) {
     const int key0 = j * kBN;
     // S^T (64 keys x 32 queries): block kb covers keys key0 + 32 kb + [0, 32).
+    // The wave's matrix work runs at raised priority, so that when the other
+    // workgroup's wave on this SIMD is in its softmax, the MFMAs are not held
+    // back behind its vector instructions.
     f32x16 s[2];
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -208,6 +222,8 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             kt + row * D + (((2 * ks + hi) ^ kswz) << 3));
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
       }
+
+    __builtin_amdgcn_s_setprio(0);
 
     // Hide future / non-existent keys (only tiles crossing the diagonal or the end).
     const bool edge = (CAUSAL && key0 + kBN - 1 > q0) || (key0 + kBN > N);
@@ -233,7 +249,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #pragma unroll
     for (int i = 2; i < 32; i += 2)
       mx = fmaxf(fmaxf(mx, s[i >> 4][i & 15]), s[(i + 1) >> 4][(i + 1) & 15]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = fmaxf(mx, other_half(mx));
 
     // m' = max(m, max S) and alpha = exp(m - m') (in log2 units); the safe
     // reference keeps a row with no visible key yet away from -inf - -inf.
@@ -306,7 +322,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   }
 
   // Epilogue: combine the two halves' normalisers, O = o / l, LSE = m + log2 l (as ln).
-  const float l_row = l + __shfl_xor(l, 32);
+  const float l_row = l + other_half(l);
   if (my_q < N) {
     const float inv = 1.f / l_row;
     float* orow = O + head + (size_t)my_q * D;
