@@ -44,6 +44,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace tiledattn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -99,6 +101,18 @@ __device__ __forceinline__ float other_half(float x) {
                                                    false);
   // lanes 0-31: pr[1] holds lanes 32-63; lanes 32-63: pr[0] holds lanes 0-31
   return __int_as_float((threadIdx.x & 32) ? pr[0] : pr[1]);
+}
+
+// Issue-order recipe for the Q K^T block (group sizes must be compile-time
+// constants, hence the expansion over an index sequence): four operand reads
+// first, then alternately one MFMA and one read, the last four MFMAs at the end.
+constexpr int kSgMfma = 0x008;
+constexpr int kSgDsRead = 0x100;
+template <int KS, int... I>
+__device__ __forceinline__ void sched_qk(std::integer_sequence<int, I...>) {
+  __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4, 0);
+  ((__builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0),
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, I < 2 * KS - 4 ? 1 : 0, 0)), ...);
 }
 
 // Workgroup -> (head, query tile).  Workgroups are handed to the 8 XCDs
@@ -222,7 +236,9 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             kt + row * D + (((2 * ks + hi) ^ kswz) << 3));
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
       }
-
+    // Issue order: the K operands of four MFMAs ahead, then one MFMA per read,
+    // so each read has ~4 MFMA times (~128 cycles) to return from LDS.
+    sched_qk<T::KS>(std::make_integer_sequence<int, 2 * T::KS>{});
     __builtin_amdgcn_s_setprio(0);
 
     // Hide future / non-existent keys (only tiles crossing the diagonal or the end).
