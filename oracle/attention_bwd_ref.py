@@ -1,0 +1,147 @@
+"""Gradients of softmax attention in float64 -- the backward parity oracle.
+
+TEST INFRASTRUCTURE ONLY (same rules as ``attention_ref``: tests, the smoke
+check and the benchmark's CPU leg may use it; the product never does; nothing
+is shared with the HIP path).
+
+What it computes (page "22. GPU Engineering: Correctness, Throughput, and
+Attention", sec. 22.5 last paragraph and sec. 22.7 derivation).  For one head
+with P = softmax(S), S = scale Q K^T (future keys hidden when causal), O = P V
+and an upstream gradient G = dL/dO:
+
+    dV = P^T G                 dP = G V^T
+    dS = P * (dP - r)          r_i = sum_j dP[i,j] P[i,j]   (a softmax row's
+                                                              Jacobian is
+                                                              diag(p) - p p^T)
+    dQ = scale dS K            dK = scale dS^T Q
+
+Functions:
+
+* ``attention_bwd_ref`` -- that definition for one head: the full probability
+  matrix from the two-pass softmax, and r from dP and P directly.
+* ``attention_bwd_tiled_ref`` -- the memory-saving method of sec. 22.7 in its
+  own steps: r taken through the output (the page shows
+  sum_j dP[i,j] P[i,j] = sum_c G[i,c] O[i,c]), each probability block
+  recomputed as exp(S - LSE) from the saved per-row log-normaliser, and the
+  three gradients accumulated block by block over a grid of query x key tiles.
+  It is pinned against the definition under many tilings.
+* ``attention_bwd_ref_batched`` -- the definition over [B, H, N, d] arrays,
+  evaluating dQ only on chosen query rows and dK, dV only on chosen key rows
+  (query rows are taken in chunks to bound memory; that only splits the sums
+  over queries into partial sums).
+
+Rows that see no key follow the lab's policy: zero probabilities, hence zero
+gradient contributions.  Inputs are the same bf16-quantised values the GPU
+receives, widened exactly to float64.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention_ref import _visible, attention_ref
+
+__all__ = ["attention_bwd_ref", "attention_bwd_tiled_ref", "attention_bwd_ref_batched"]
+
+
+def _as64(*xs):
+    return tuple(np.asarray(x, dtype=np.float64) for x in xs)
+
+
+def _softmax_rows(q, k, scale, causal, query_offset, rows):
+    """P[rows, :] by the two-pass definition; rows with no visible key -> 0."""
+    s = float(scale) * (q[rows] @ k.T)
+    s = np.where(_visible(q.shape[0], k.shape[0], causal, query_offset, rows), s, -np.inf)
+    m = s.max(axis=1) if k.shape[0] else np.full(len(rows), -np.inf)
+    live = np.isfinite(m)
+    p = np.exp(s - np.where(live, m, 0.0)[:, None])
+    p[~live] = 0.0
+    p[live] /= p[live].sum(axis=1, keepdims=True)
+    return p
+
+
+def _check(q, k, v, do):
+    if q.ndim != 2 or k.ndim != 2 or v.ndim != 2 or do.ndim != 2:
+        raise ValueError("q, k, v, dO must be rank 2 for one head")
+    if q.shape[1] != k.shape[1] or k.shape[0] != v.shape[0]:
+        raise ValueError("incompatible q/k/v shapes")
+    if do.shape != (q.shape[0], v.shape[1]):
+        raise ValueError("dO must be [Nq, dv]")
+
+
+def attention_bwd_ref(q, k, v, do, scale: float, causal: bool = False, query_offset: int = 0):
+    """(dQ, dK, dV) of a loss L with dL/dO = ``do``, one head, float64.
+
+    q: [Nq, d], k: [Nk, d], v: [Nk, dv], do: [Nq, dv].
+    """
+    q, k, v, do = _as64(q, k, v, do)
+    _check(q, k, v, do)
+    p = _softmax_rows(q, k, scale, causal, query_offset, np.arange(q.shape[0]))
+    dv = p.T @ do
+    dp = do @ v.T
+    r = (dp * p).sum(axis=1, keepdims=True)
+    ds = p * (dp - r)
+    return float(scale) * (ds @ k), float(scale) * (ds.T @ q), dv
+
+
+def attention_bwd_tiled_ref(q, k, v, do, scale: float, q_bounds, k_bounds,
+                            causal: bool = False, query_offset: int = 0):
+    """The recomputing backward of sec. 22.7 over query tiles [q_bounds[a], q_bounds[a+1])
+    times key tiles [k_bounds[b], k_bounds[b+1]).  Never forms more than one
+    probability block at a time."""
+    q, k, v, do = _as64(q, k, v, do)
+    _check(q, k, v, do)
+    out, lse = attention_ref(q, k, v, scale, causal, query_offset=query_offset)
+    r_all = np.einsum("ic,ic->i", do, out)          # sum_c G[i,c] O[i,c]
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for q0, q1 in zip(q_bounds[:-1], q_bounds[1:]):
+        live = np.isfinite(lse[q0:q1])
+        log_norm = np.where(live, lse[q0:q1], 0.0)
+        qpos = np.arange(q0, q1) + query_offset
+        for k0, k1 in zip(k_bounds[:-1], k_bounds[1:]):
+            s = float(scale) * (q[q0:q1] @ k[k0:k1].T)
+            if causal:
+                s[np.arange(k0, k1)[None, :] > qpos[:, None]] = -np.inf
+            p = np.exp(s - log_norm[:, None])        # this block of P, rebuilt
+            p[~live] = 0.0
+            ds = p * (do[q0:q1] @ v[k0:k1].T - r_all[q0:q1, None])
+            dv[k0:k1] += p.T @ do[q0:q1]
+            dk[k0:k1] += float(scale) * (ds.T @ q[q0:q1])
+            dq[q0:q1] += float(scale) * (ds @ k[k0:k1])
+    return dq, dk, dv
+
+
+def attention_bwd_ref_batched(q, k, v, do, scale: float, causal: bool = False,
+                              query_rows=None, key_rows=None, heads=None, chunk: int = 1024):
+    """The definition over [B, H, N, d] inputs (self-attention, query_offset 0).
+
+    query_rows / key_rows: None (all rows) or 1-D integer arrays used for every
+    evaluated head.  heads: None (all B*H heads) or a list of flat head indices
+    b*H + h.  Returns (dQ [nh, Rq, d], dK [nh, Rk, d], dV [nh, Rk, dv]) for the
+    evaluated heads in the given order.
+    """
+    q, k, v, do = (np.asarray(x) for x in (q, k, v, do))
+    if q.ndim != 4:
+        raise ValueError("expected [B, H, N, d]")
+    B, H, N, _ = q.shape
+    heads = list(range(B * H)) if heads is None else list(heads)
+    qr = np.arange(N) if query_rows is None else np.asarray(query_rows, dtype=np.int64)
+    kr = np.arange(N) if key_rows is None else np.asarray(key_rows, dtype=np.int64)
+    dv_dim = v.shape[-1]
+    dq = np.zeros((len(heads), qr.size, q.shape[-1]))
+    dk = np.zeros((len(heads), kr.size, k.shape[-1]))
+    dvo = np.zeros((len(heads), kr.size, dv_dim))
+    for n, flat in enumerate(heads):
+        b, h = divmod(flat, H)
+        qh, kh, vh, gh = _as64(q[b, h], k[b, h], v[b, h], do[b, h])
+        _check(qh, kh, vh, gh)
+        for c0 in range(0, N, chunk):
+            rows = np.arange(c0, min(N, c0 + chunk))
+            p = _softmax_rows(qh, kh, scale, causal, 0, rows)
+            dp = gh[rows] @ vh.T
+            ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))
+            dvo[n] += p[:, kr].T @ gh[rows]
+            dk[n] += float(scale) * (ds[:, kr].T @ qh[rows])
+            sel = (qr >= c0) & (qr < rows[-1] + 1)
+            if sel.any():
+                dq[n, sel] = float(scale) * (ds[qr[sel] - c0] @ kh)
+    return dq, dk, dvo
