@@ -1,6 +1,6 @@
 /*
- * tiledattn.h -- C ABI of the fused attention-forward library for AMD
- * Instinct MI355X (gfx950).  Library file: libtiledattn.so.
+ * tiledattn.h -- C ABI of the fused attention library (forward and backward)
+ * for AMD Instinct MI355X (gfx950).  Library file: libtiledattn.so.
  *
  * The operation is softmax attention with an online (tiled) softmax: for
  * every (batch, head) and query row i,
@@ -22,6 +22,8 @@
  */
 #ifndef TILEDATTN_H
 #define TILEDATTN_H
+
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -67,6 +69,54 @@ typedef enum {
  */
 int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
              int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * attn_bwd_workspace_size -- bytes of device workspace attn_bwd needs for
+ * (B, H, N): 8 * B * H * (N rounded up to even).  Returns 0 when the sizes are
+ * out of the range attn_bwd accepts.
+ */
+size_t attn_bwd_workspace_size(int B, int H, int N);
+
+/*
+ * attn_bwd -- enqueue the gradients of attn_fwd on `stream`.
+ *
+ * For a loss L with G = dL/dO, with P the softmax of the scaled (and masked)
+ * scores of each row:
+ *
+ *     dV = P^T G,   dP = G V^T,   dS = P * (dP - D),   D_i = sum_c G[i,c] O[i,c]
+ *     dQ = scale dS K,   dK = scale dS^T Q
+ *
+ * (page "22. GPU Engineering: Correctness, Throughput, and Attention",
+ * sec. 22.5 for the formulas, sec. 22.7 for the derivation: the row sum of
+ * dP * P equals D, so only O and the per-row log-normaliser are kept from the
+ * forward, and every probability block is recomputed as exp(S - LSE)).
+ *
+ *   q, k, v   : device, bfloat16, [B, H, N, d] -- the forward's inputs. Read only.
+ *   o, lse    : device, float32, [B, H, N, d] and [B, H, N] -- the forward's
+ *               outputs for the same q, k, v, scale and causal flag.  Read only.
+ *   dout      : device, bfloat16, [B, H, N, d] -- G, the gradient of the loss
+ *               with respect to O, given at the precision of the matrix-unit
+ *               operands.  Read only.
+ *   dq, dk, dv: device, float32, [B, H, N, d], written (every element).
+ *   workspace : device, attn_bwd_workspace_size(B, H, N) bytes, 16-byte
+ *               aligned, owned by the caller; overwritten (per-row D and
+ *               LSE log2(e)).  Calls that run concurrently need separate
+ *               workspaces.
+ *   B, H, N, d, scale, causal, stream: as for attn_fwd.
+ *
+ * Every gradient row is written by exactly one workgroup (no atomics): the
+ * result is deterministic, bit for bit, for a given input.
+ *
+ * Ownership and synchronisation as for attn_fwd: nothing is allocated or kept;
+ * the call only enqueues.  Outputs must not overlap any input or each other.
+ *
+ * Errors: as for attn_fwd; q, k, v, o, dout, dq, dk, dv and workspace need
+ * 16-byte alignment, lse 4 bytes (TA_ERR_MISALIGNED otherwise).
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const float* o,
+             const float* lse, const void* dout, float* dq, float* dk, float* dv,
+             void* workspace, int B, int H, int N, int d, float scale, int causal,
+             void* stream);
 
 /* Human-readable text for a ta_status value (static storage; never NULL). */
 const char* attn_status_string(int status);

@@ -40,7 +40,8 @@ def declared_functions():
 
 
 def test_header_declares_entry_points():
-    assert declared_functions() == ["attn_fwd", "attn_status_string"]
+    assert declared_functions() == ["attn_bwd", "attn_bwd_workspace_size", "attn_fwd",
+                                    "attn_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -107,3 +108,59 @@ def test_ctypes_signature():
     lib = ta.load_library()
     assert lib.attn_fwd.restype is ctypes.c_int
     assert len(lib.attn_fwd.argtypes) == 12
+    assert lib.attn_bwd.restype is ctypes.c_int
+    assert len(lib.attn_bwd.argtypes) == 17
+
+
+# ---- backward entry point -------------------------------------------------
+
+BWD_PTRS = ["q", "k", "v", "o", "lse", "do", "dq", "dk", "dv", "ws"]
+
+
+def call_bwd(**over):
+    args = dict({p: A for p in BWD_PTRS}, B=1, H=1, N=128, d=64, scale=0.125, causal=0)
+    args.update(over)
+    return ta.attn_bwd_raw(*(args[p] for p in BWD_PTRS), args["B"], args["H"], args["N"],
+                           args["d"], args["scale"], args["causal"], 0)
+
+
+def test_workspace_size():
+    assert ta.attn_bwd_workspace_size(2, 32, 8192) == 2 * 32 * 8192 * 8
+    assert ta.attn_bwd_workspace_size(1, 1, 1003) == 1004 * 8    # rows padded to even
+    assert ta.attn_bwd_workspace_size(3, 5, 1) == 15 * 2 * 8
+    assert ta.attn_bwd_workspace_size(0, 1, 8) == 0
+    assert ta.attn_bwd_workspace_size(1, 1, (1 << 22) + 1) == 0
+
+
+@host_only
+@pytest.mark.parametrize("field", BWD_PTRS)
+def test_bwd_null_pointer(field):
+    assert call_bwd(**{field: 0}) == ta.TA_ERR_INVALID_ARG
+
+
+@host_only
+@pytest.mark.parametrize("over", [dict(B=0), dict(H=0), dict(N=0), dict(N=(1 << 22) + 1),
+                                  dict(causal=2), dict(scale=math.nan), dict(scale=math.inf),
+                                  dict(B=1 << 16, H=1 << 15, N=1 << 20)])
+def test_bwd_invalid_sizes_flags_scale(over):
+    assert call_bwd(**over) == ta.TA_ERR_INVALID_ARG
+
+
+@host_only
+@pytest.mark.parametrize("d", [0, 32, 96, 256])
+def test_bwd_unsupported_head_dim(d):
+    assert call_bwd(d=d) == ta.TA_ERR_UNSUPPORTED
+
+
+@host_only
+@pytest.mark.parametrize("field,off", [(p, 8) for p in BWD_PTRS if p != "lse"] + [("lse", 2)])
+def test_bwd_misaligned(field, off):
+    assert call_bwd(**{field: A + off}) == ta.TA_ERR_MISALIGNED
+
+
+def test_python_bwd_wrapper_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    o = torch.zeros(1, 1, 8, 64)
+    with pytest.raises(ValueError):
+        ta.attn_bwd(x, x, x, o, torch.zeros(1, 1, 8), x)

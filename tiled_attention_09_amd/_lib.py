@@ -34,6 +34,11 @@ def load_library() -> ctypes.CDLL:
         lib.attn_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
         lib.attn_fwd.restype = ctypes.c_int
+        lib.attn_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 4 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+        lib.attn_bwd.restype = ctypes.c_int
+        lib.attn_bwd_workspace_size.argtypes = [ctypes.c_int] * 3
+        lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
         lib.attn_status_string.argtypes = [ctypes.c_int]
         lib.attn_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -87,3 +92,67 @@ def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None
     if st != TA_OK:
         raise RuntimeError("attn_fwd failed: %s (status %d)" % (attn_status_string(st), st))
     return out, lse
+
+
+def attn_bwd_workspace_size(B: int, H: int, N: int) -> int:
+    """Bytes of device workspace ``attn_bwd`` needs (0 if the sizes are out of range)."""
+    return int(load_library().attn_bwd_workspace_size(B, H, N))
+
+
+def attn_bwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, do_ptr: int,
+                 dq_ptr: int, dk_ptr: int, dv_ptr: int, ws_ptr: int, B: int, H: int, N: int,
+                 d: int, scale: float, causal: int, stream: int = 0) -> int:
+    """Call the C entry point with raw addresses; returns the ta_status code."""
+    return load_library().attn_bwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr,
+                                   dv_ptr, ws_ptr, B, H, N, d, ctypes.c_float(scale), causal,
+                                   stream)
+
+
+def attn_bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False,
+             workspace=None, grads=None, stream=None):
+    """Gradients of ``attn_fwd`` on the GPU.
+
+    q, k, v, do: bfloat16 [B, H, N, d]; o float32 [B, H, N, d] and lse float32
+    [B, H, N] from ``attn_fwd`` with the same scale and causal flag.  Returns
+    (dq, dk, dv), float32 [B, H, N, d].  ``workspace`` (a uint8 device tensor of
+    at least ``attn_bwd_workspace_size`` bytes) and ``grads`` (three float32
+    tensors) may be given to reuse buffers.
+    """
+    import torch
+    lib = load_library()
+    for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16),
+                        ("v", v, torch.bfloat16), ("do", do, torch.bfloat16),
+                        ("o", o, torch.float32)):
+        if not t.is_cuda:
+            raise ValueError("%s must be a device tensor" % name)
+        if t.dtype != dt:
+            raise ValueError("%s must be %s" % (name, dt))
+        if t.dim() != 4 or t.shape != q.shape or not t.is_contiguous():
+            raise ValueError("%s must be contiguous with q's shape [B, H, N, d]" % name)
+    B, H, N, d = (int(x) for x in q.shape)
+    if not lse.is_cuda or lse.dtype != torch.float32 or lse.shape != (B, H, N) \
+            or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 device tensor [B, H, N]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    ws_bytes = attn_bwd_workspace_size(B, H, N)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    if workspace.numel() * workspace.element_size() < ws_bytes or not workspace.is_cuda:
+        raise ValueError("workspace must be a device buffer of at least %d bytes" % ws_bytes)
+    if grads is None:
+        grads = tuple(torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+                      for _ in range(3))
+    for t in grads:
+        if t.shape != (B, H, N, d) or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("grads must be contiguous float32 [B, H, N, d]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    dq, dk, dv = grads
+    st = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                      do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                      workspace.data_ptr(), B, H, N, d, ctypes.c_float(float(scale)),
+                      int(bool(causal)), int(stream))
+    if st != TA_OK:
+        raise RuntimeError("attn_bwd failed: %s (status %d)" % (attn_status_string(st), st))
+    return dq, dk, dv

@@ -15,7 +15,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "attn_fwd.hip")
+SRCS = [os.path.join(HERE, "csrc", f) for f in ("attn_fwd.hip", "attn_bwd.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libtiledattn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
@@ -39,7 +39,7 @@ def hipcc() -> str:
 def build_library(extra_flags=(), verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     tmp = OUT + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + list(extra_flags) + ["-I", INCLUDE, SRC, "-o", tmp]
+    cmd = [hipcc()] + HIPCC_FLAGS + list(extra_flags) + ["-I", INCLUDE] + SRCS + ["-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     report = os.path.join(BUILD_DIR, "resource_usage.txt")
     with open(report, "w") as f:

@@ -1,0 +1,425 @@
+// Attention backward for gfx950 (MI355X): recomputing probabilities from the
+// saved per-row log-normaliser, never storing the N x N score matrix.
+//
+// Method (page "22. GPU Engineering: Correctness, Throughput, and Attention",
+// sec. 22.5 and the derivation of sec. 22.7).  With G = dL/dO:
+//   dV = P^T G,   dP = G V^T,   dS = P * (dP - D),   D_i = sum_c G[i,c] O[i,c]
+//   dQ = scale dS K,   dK = scale dS^T Q,
+// where D replaces the row sum of dP * P by the identity the page derives, and
+// each block of P is rebuilt as exp(S - LSE).  Base-2 exponentials: with
+// c = scale log2(e) and LSE2 = LSE log2(e), P = 2^(c (q.k) - LSE2).
+//
+// Three kernels, all on the caller's stream:
+//  1. attn_bwd_prep_kernel: per row, D and LSE2 into a workspace of float2
+//     {LSE2, D}, each head's rows padded to an even count so every head starts
+//     16-byte aligned (HBM-bound, one pass over O and G).
+//  2. attn_bwd_dkdv_kernel: one workgroup owns 128 keys of one head (32 per
+//     wave) and streams that head's query rows in tiles of 64; the wave's dK
+//     and dV rows stay in registers for the whole loop and are written once,
+//     so no two workgroups ever add into the same gradient row (the parallel
+//     dK/dV accumulation the page asks for, without atomics).
+//  3. attn_bwd_dq_kernel: one workgroup owns 128 query rows (32 per wave) and
+//     streams the keys and values in tiles of 64, like the forward; dQ stays
+//     in registers.  Recomputing S and dP here instead of adding dQ partial
+//     sums atomically from kernel 2 costs two extra products per tile but
+//     keeps every gradient deterministic.
+//
+// Operand layout (CDNA4 MFMA 32x32x16 bf16, fp32 accumulation; lane = l):
+//  * dK/dV kernel: S = Q K^T and dP = G V^T for 32 queries x the wave's 32
+//    keys per accumulator block, so every lane owns one key column (l % 32)
+//    and 16 query rows; K and V of the wave's keys stay in VGPRs as B
+//    operands; Q and G rows are read from LDS as A operands.  P and dS, rounded
+//    to bf16, are then directly the B operands (k = query) of
+//    dV^T += G^T P and dK^T += Q^T dS, with G^T and Q^T read from the same LDS
+//    tiles by the transpose read.  LSE2 and D of the 16 query rows a lane
+//    holds come from a 512-byte LDS copy of the tile's workspace rows.
+//  * dQ kernel: the forward's orientation, S^T = K Q^T and dP^T = V G^T, so a
+//    lane owns one query (one LSE2 and D in registers) and dS^T is the B
+//    operand of dQ^T += K^T dS^T, K^T by the transpose read.
+//  * Tiles reach LDS by buffer_load ... lds copies two stages deep (one
+//    barrier per tile), in the swizzled layout of attn_common.hpp.  Rows past
+//    the end of a head read as zeros.
+//  * Causal: a key tile starts at the first query tile that can see it; the
+//    query tiles end at the last key tile they can see; a wave whose rows lie
+//    entirely on the hidden side of a tile skips its math; element masks only
+//    on tiles crossing the diagonal or the end of the sequence.
+#pragma once
+
+#include "attn_common.hpp"
+
+namespace tiledattn {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kPrepRowsPerBlock = 16;     // 16 lanes per row, 256 threads
+
+// Copy the {LSE2, D} pairs of the 64 query rows of tile i (512 bytes) into LDS:
+// lanes 0..31 of wave 0, 16 bytes each.
+__device__ __forceinline__ void issue_stats(__amdgpu_buffer_rsrc_t sr, int i, int wave, int lane,
+                                            TA_LDS float* sd) {
+  if (wave == 0 && lane < 32)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (TA_LDS void*)sd, 16, (uint32_t)lane * 16u,
+                                             (uint32_t)i * (kBN * 8u), 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// 1. D_i = sum_c G[i,c] O[i,c] and LSE2_i = LSE_i log2(e), one row per 16 lanes.
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const float* __restrict__ O,
+                                                            const uint16_t* __restrict__ G,
+                                                            const float* __restrict__ LSE,
+                                                            f32x2* __restrict__ stats, int N,
+                                                            int stats_stride, int64_t rows) {
+  constexpr int E = D / 16;                      // values per lane: 8 (d=128) or 4 (d=64)
+  const int sub = threadIdx.x & 15;
+  const int64_t row = (int64_t)blockIdx.x * kPrepRowsPerBlock + (threadIdx.x >> 4);
+  float acc = 0.f;
+  if (row < rows) {
+    const float* orow = O + row * D + sub * E;
+    const uint32_t* grow = reinterpret_cast<const uint32_t*>(G + row * D + sub * E);
+#pragma unroll
+    for (int e = 0; e < E; e += 4) {
+      const f32x4 o = *reinterpret_cast<const f32x4*>(orow + e);
+      const uint32_t w0 = grow[e / 2], w1 = grow[e / 2 + 1];   // 4 bf16, little-endian pairs
+      acc = __builtin_fmaf(__uint_as_float(w0 << 16), o[0], acc);
+      acc = __builtin_fmaf(__uint_as_float(w0 & 0xffff0000u), o[1], acc);
+      acc = __builtin_fmaf(__uint_as_float(w1 << 16), o[2], acc);
+      acc = __builtin_fmaf(__uint_as_float(w1 & 0xffff0000u), o[3], acc);
+    }
+  }
+  // Sum over the 16 lanes of the row (xor butterfly stays inside the group).
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
+  if (row < rows && sub == 0) {
+    const int64_t bh = row / N;
+    f32x2 st;
+    st[0] = LSE[row] * kLog2e;
+    st[1] = acc;
+    stats[bh * stats_stride + (row - bh * N)] = st;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. dK and dV for 128 keys of one head per workgroup.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
+void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                          const uint16_t* __restrict__ V, const uint16_t* __restrict__ G,
+                          const f32x2* __restrict__ stats, float* __restrict__ dK,
+                          float* __restrict__ dV, int bh_count, int N, int stats_stride,
+                          int n_kt, float c, float scale) {
+  using T = Tile<D>;
+  __shared__ __attribute__((aligned(1024))) uint16_t q_lds0[kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t g_lds0[kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t q_lds1[kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t g_lds1[kBN * D];
+  __shared__ __attribute__((aligned(16))) float st_lds0[2 * kBN];   // {LSE2, D} per query row
+  __shared__ __attribute__((aligned(16))) float st_lds1[2 * kBN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  int bh, kt;
+  map_block(blockIdx.x, bh_count, n_kt, false, bh, kt);   // causal: key tile 0 (most work) first
+
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2u;
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t gr = make_rsrc(G + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(stats + (size_t)bh * stats_stride, (uint32_t)N * 8u);
+
+  const int k0 = kt * kBM + wave * 32;    // first key of this wave
+  const int my_k = k0 + l32;              // this lane's key
+
+  // K and V rows of the wave's keys (B operands, k = d): [my_k][16 ks + 8 hi + 0..7].
+  bf16x8 kf[T::KS], vf[T::KS];
+#pragma unroll
+  for (int ks = 0; ks < T::KS; ++ks) {
+    const uint32_t off = (uint32_t)(my_k * D + 16 * ks + 8 * hi) * 2u;
+    kf[ks] = __builtin_bit_cast(bf16x8, load16(kr, off));
+    vf[ks] = __builtin_bit_cast(bf16x8, load16(vr, off));
+  }
+
+  uint32_t src_off[T::LOADS];
+  tile_src_offsets<D>(src_off, wave, lane);
+  const int rswz = T::swz(l32);
+  const int row_lo = 4 * hi + ((lane & 15) >> 2);              // transpose-read source row
+  const int col_lo = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // transpose-read source column
+
+  f32x16 dk[T::DB], dv[T::DB];
+#pragma unroll
+  for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dk[db][i] = 0.f;
+      dv[db][i] = 0.f;
+    }
+
+  const int n_qt = (N + kBN - 1) / kBN;
+  const int i0 = CAUSAL ? (kt * kBM) / kBN : 0;   // first query tile that sees any key here
+
+  auto compute_tile = [&](int i, const TA_LDS uint16_t* qt, const TA_LDS uint16_t* gt,
+                          const TA_LDS float* st) {
+    const int qbase = i * kBN;
+    // S and dP: 2 blocks of 32 queries x the wave's 32 keys.
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        s[qb][e] = 0.f;
+        dp[qb][e] = 0.f;
+      }
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const bf16x8 aq = read_rows<D>(qt, qb * 32 + l32, ks, hi, rswz);
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ks], s[qb], 0, 0, 0);
+      }
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const bf16x8 ag = read_rows<D>(gt, qb * 32 + l32, ks, hi, rswz);
+        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, vf[ks], dp[qb], 0, 0, 0);
+      }
+
+    // P = 2^(c s - LSE2) and dS = P (dP - D); element e of block qb is query
+    // qbase + 32 qb + 8 (e / 4) + 4 hi + e % 4 of key my_k.
+    const bool edge = (CAUSAL && qbase < k0 + 31) || (qbase + kBN > N);
+    bf16x8 pf[4], sf[4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int qrow = 32 * qb + 8 * g4 + 4 * hi;          // tile row of element 4 g4
+        const f32x4 sa = *reinterpret_cast<const TA_LDS f32x4*>(st + 2 * qrow);
+        const f32x4 sb = *reinterpret_cast<const TA_LDS f32x4*>(st + 2 * qrow + 4);
+        const float lse2[4] = {sa[0], sa[2], sb[0], sb[2]};
+        const float dd[4] = {sa[1], sa[3], sb[1], sb[3]};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int e = 4 * g4 + t;
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][e], c, -lse2[t]));
+          if (edge) {
+            const int q = qbase + qrow + t;
+            if ((CAUSAL && my_k > q) || q >= N) p = 0.f;
+          }
+          const float ds = p * (dp[qb][e] - dd[t]);
+          pf[2 * qb + (e >> 3)][e & 7] = (__bf16)p;
+          sf[2 * qb + (e >> 3)][e & 7] = (__bf16)ds;
+        }
+      }
+
+    // dV^T (d x 32 keys) += G^T (d x 64 queries) P;  dK^T += Q^T dS.
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db) {
+        const bf16x8 ag = read_cols<D>(gt, g, db, row_lo, col_lo);
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, pf[g], dv[db], 0, 0, 0);
+        const bf16x8 aq = read_cols<D>(qt, g, db, row_lo, col_lo);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sf[g], dk[db], 0, 0, 0);
+      }
+  };
+
+  TA_LDS uint16_t* const q0p = (TA_LDS uint16_t*)q_lds0;
+  TA_LDS uint16_t* const g0p = (TA_LDS uint16_t*)g_lds0;
+  TA_LDS uint16_t* const q1p = (TA_LDS uint16_t*)q_lds1;
+  TA_LDS uint16_t* const g1p = (TA_LDS uint16_t*)g_lds1;
+  TA_LDS float* const s0p = (TA_LDS float*)st_lds0;
+  TA_LDS float* const s1p = (TA_LDS float*)st_lds1;
+  // A wave's keys are all hidden from query tile i when its last query
+  // precedes the wave's first key.
+  auto active = [&](int i) { return !(CAUSAL && i * kBN + kBN - 1 < k0); };
+  // Each stage holds the Q and G rows of one query tile and their {LSE2, D}.
+  if (i0 < n_qt) {
+    issue_tile<D>(qr, gr, src_off, i0, wave, q0p, g0p);
+    issue_stats(sr, i0, wave, lane, s0p);
+  }
+  for (int i = i0; i < n_qt; i += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();                       // tile i visible; tile i-1's readers done
+    if (i + 1 < n_qt) {
+      issue_tile<D>(qr, gr, src_off, i + 1, wave, q1p, g1p);
+      issue_stats(sr, i + 1, wave, lane, s1p);
+    }
+    if (active(i)) compute_tile(i, q0p, g0p, s0p);
+    if (i + 1 >= n_qt) break;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (i + 2 < n_qt) {
+      issue_tile<D>(qr, gr, src_off, i + 2, wave, q0p, g0p);
+      issue_stats(sr, i + 2, wave, lane, s0p);
+    }
+    if (active(i + 1)) compute_tile(i + 1, q1p, g1p, s1p);
+  }
+
+  // Epilogue: lane owns key my_k; accumulator element e of block db is column
+  // 32 db + 8 (e / 4) + 4 hi + e % 4.
+  if (my_k < N) {
+    float* dkrow = dK + head + (size_t)my_k * D;
+    float* dvrow = dV + head + (size_t)my_k * D;
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 a = {dk[db][4 * g] * scale, dk[db][4 * g + 1] * scale, dk[db][4 * g + 2] * scale,
+                   dk[db][4 * g + 3] * scale};
+        f32x4 b = {dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]};
+        *reinterpret_cast<f32x4*>(dkrow + db * 32 + 8 * g + 4 * hi) = a;
+        *reinterpret_cast<f32x4*>(dvrow + db * 32 + 8 * g + 4 * hi) = b;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. dQ for 128 query rows of one head per workgroup.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                        const uint16_t* __restrict__ V, const uint16_t* __restrict__ G,
+                        const f32x2* __restrict__ stats, float* __restrict__ dQ, int bh_count,
+                        int N, int stats_stride, int n_qt, float c, float scale) {
+  using T = Tile<D>;
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[kBN * D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  int bh, qt;
+  map_block(blockIdx.x, bh_count, n_qt, CAUSAL, bh, qt);
+
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2u;
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t gr = make_rsrc(G + head, head_bytes);
+
+  const int q0 = qt * kBM + wave * 32;
+  const int my_q = q0 + l32;
+
+  // Q and G rows of the lane's query (B operands of S^T = K Q^T, dP^T = V G^T).
+  bf16x8 qf[T::KS], gf[T::KS];
+#pragma unroll
+  for (int ks = 0; ks < T::KS; ++ks) {
+    const uint32_t off = (uint32_t)(my_q * D + 16 * ks + 8 * hi) * 2u;
+    qf[ks] = __builtin_bit_cast(bf16x8, load16(qr, off));
+    gf[ks] = __builtin_bit_cast(bf16x8, load16(gr, off));
+  }
+  float lse2 = 0.f, dd = 0.f;
+  if (my_q < N) {
+    const f32x2 st = stats[(size_t)bh * stats_stride + my_q];
+    lse2 = st[0];
+    dd = st[1];
+  }
+
+  uint32_t src_off[T::LOADS];
+  tile_src_offsets<D>(src_off, wave, lane);
+  const int rswz = T::swz(l32);
+  const int row_lo = 4 * hi + ((lane & 15) >> 2);
+  const int col_lo = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  f32x16 dq[T::DB];
+#pragma unroll
+  for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dq[db][i] = 0.f;
+
+  const int n_kt_all = (N + kBN - 1) / kBN;
+  const int n_kt = CAUSAL ? min(n_kt_all, (qt + 1) * (kBM / kBN)) : n_kt_all;
+
+  auto compute_tile = [&](int j, const TA_LDS uint16_t* kt, const TA_LDS uint16_t* vt) {
+    const int key0 = j * kBN;
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        s[kb][e] = 0.f;
+        dp[kb][e] = 0.f;
+      }
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 ak = read_rows<D>(kt, kb * 32 + l32, ks, hi, rswz);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[ks], s[kb], 0, 0, 0);
+      }
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 av = read_rows<D>(vt, kb * 32 + l32, ks, hi, rswz);
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, gf[ks], dp[kb], 0, 0, 0);
+      }
+
+    // Element e of block kb is key key0 + 32 kb + 8 (e / 4) + 4 hi + e % 4 of query my_q.
+    const bool edge = (CAUSAL && key0 + kBN - 1 > q0) || (key0 + kBN > N);
+    bf16x8 sf[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e], c, -lse2));
+        if (edge) {
+          const int key = key0 + kb * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+          if ((CAUSAL && key > my_q) || key >= N) p = 0.f;
+        }
+        sf[2 * kb + (e >> 3)][e & 7] = (__bf16)(p * (dp[kb][e] - dd));
+      }
+
+    // dQ^T (d x 32 queries) += K^T (d x 64 keys) dS^T (64 keys x 32 queries).
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db) {
+        const bf16x8 ak = read_cols<D>(kt, g, db, row_lo, col_lo);
+        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, sf[g], dq[db], 0, 0, 0);
+      }
+  };
+
+  TA_LDS uint16_t* const k0p = (TA_LDS uint16_t*)k_lds0;
+  TA_LDS uint16_t* const v0p = (TA_LDS uint16_t*)v_lds0;
+  TA_LDS uint16_t* const k1p = (TA_LDS uint16_t*)k_lds1;
+  TA_LDS uint16_t* const v1p = (TA_LDS uint16_t*)v_lds1;
+  issue_tile<D>(kr, vr, src_off, 0, wave, k0p, v0p);
+  for (int j = 0; j < n_kt; j += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (j + 1 < n_kt) issue_tile<D>(kr, vr, src_off, j + 1, wave, k1p, v1p);
+    if (!(CAUSAL && j * kBN > q0 + 31)) compute_tile(j, k0p, v0p);
+    if (j + 1 >= n_kt) break;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (j + 2 < n_kt) issue_tile<D>(kr, vr, src_off, j + 2, wave, k0p, v0p);
+    if (!(CAUSAL && (j + 1) * kBN > q0 + 31)) compute_tile(j + 1, k1p, v1p);
+  }
+
+  if (my_q < N) {
+    float* row = dQ + head + (size_t)my_q * D;
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 a = {dq[db][4 * g] * scale, dq[db][4 * g + 1] * scale, dq[db][4 * g + 2] * scale,
+                   dq[db][4 * g + 3] * scale};
+        *reinterpret_cast<f32x4*>(row + db * 32 + 8 * g + 4 * hi) = a;
+      }
+  }
+}
+
+}  // namespace tiledattn

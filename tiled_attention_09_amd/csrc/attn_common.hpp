@@ -1,0 +1,164 @@
+// Building blocks shared by the attention kernels for gfx950 (MI355X): vector
+// types, the LDS tile of 64 rows x d with its XOR swizzle, buffer resources,
+// the direct HBM/L2 -> LDS tile copy, the half-wave exchange and the
+// XCD-aware workgroup order.
+//
+// LDS tile: 64 rows of d bf16 values, row-major, the 16-byte chunks of row r
+// stored at chunk index (c ^ swz(r)).  Row-wise operand reads (16 consecutive
+// rows per 16 lanes) and LDS transpose reads (4 rows per half-wave) are then
+// free of bank conflicts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <utility>
+
+namespace tiledattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kWaves = 4;
+constexpr int kThreads = kWave * kWaves;
+constexpr int kBM = 128;          // rows owned by one workgroup (32 per wave)
+constexpr int kBN = 64;           // rows per LDS tile
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
+constexpr float kLn2 = 0.69314718055994530942f;
+
+#define TA_LDS __attribute__((address_space(3)))
+
+template <int D>
+struct Tile {
+  static_assert(D == 64 || D == 128, "head dim");
+  static constexpr int KS = D / 16;                 // MFMA k-steps over d for S^T
+  static constexpr int DB = D / 32;                 // 32-row blocks of O^T
+  static constexpr int DCH = D / 8;                 // 16-byte chunks per key row
+  static constexpr int BYTES = kBN * D * 2;         // one tile
+  static constexpr int LOADS = BYTES / (kThreads * 16);   // 16-byte loads per thread per tile
+  static_assert(LOADS * kThreads * 16 == BYTES, "tile split");
+
+  // XOR applied to the chunk index of key row r.  d=128 (16 chunks): bijective
+  // on any 16 aligned rows, and rows 4a..4a+3 get 4 different 64-byte groups.
+  // d=64 (8 chunks, two rows per 256-byte bank window): bijective on the rows
+  // of one parity within 16 rows, and rows 4a, 4a+2 (and 4a+1, 4a+3) get
+  // different 64-byte groups.
+  __device__ static __forceinline__ int swz(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  }
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+// Both halves of a wave hold partial results for the same 32 queries; the
+// swap (v_permlane32_swap) gives every lane the other half's value without a
+// trip through LDS.
+__device__ __forceinline__ float other_half(float x) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false,
+                                                   false);
+  // lanes 0-31: pr[1] holds lanes 32-63; lanes 32-63: pr[0] holds lanes 0-31
+  return __int_as_float((threadIdx.x & 32) ? pr[0] : pr[1]);
+}
+
+// Issue-order recipe for the Q K^T block (group sizes must be compile-time
+// constants, hence the expansion over an index sequence): four operand reads
+// first, then alternately one MFMA and one read, the last four MFMAs at the end.
+constexpr int kSgMfma = 0x008;
+constexpr int kSgDsRead = 0x100;
+template <int KS, int... I>
+__device__ __forceinline__ void sched_qk(std::integer_sequence<int, I...>) {
+  __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4, 0);
+  ((__builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0),
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, I < 2 * KS - 4 ? 1 : 0, 0)), ...);
+}
+
+// Workgroup -> (head, row tile).  Workgroups are handed to the 8 XCDs
+// round-robin, so block b runs on XCD b % 8; consecutive logical indices are
+// given to the same XCD so one head's tiles share that XCD's L2.  With
+// `reverse` the tiles of a head are taken last to first (causal query tiles:
+// the longest go first).
+__device__ __forceinline__ void map_block(int bid, int bh_count, int n_t, bool reverse,
+                                          int& bh, int& t_out) {
+  const int total = bh_count * n_t;
+  int j = bid;
+  if ((total & 7) == 0) j = (bid & 7) * (total >> 3) + (bid >> 3);
+  bh = j / n_t;
+  const int t = j - bh * n_t;
+  t_out = reverse ? n_t - 1 - t : t;
+}
+
+// Enqueue the copy of row tile j of two matrices (K and V; Q and dO) into one
+// LDS stage.  Load i of wave w fills bytes [(4 i + w) * 1024, +1024) of the
+// stage's tile, one 16-byte chunk per lane; src_off holds each lane's offset
+// within a tile (tile_src_offsets).
+template <int D>
+__device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                           const uint32_t* src_off, int j, int wave,
+                                           TA_LDS uint16_t* kd, TA_LDS uint16_t* vd) {
+  const uint32_t tile_off = (uint32_t)j * (uint32_t)Tile<D>::BYTES;   // scalar
+#pragma unroll
+  for (int i = 0; i < Tile<D>::LOADS; ++i) {
+    const int dst = (4 * i + wave) * 512;   // uint16 elements, wave-uniform
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (TA_LDS void*)(kd + dst), 16, src_off[i],
+                                             tile_off, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (TA_LDS void*)(vd + dst), 16, src_off[i],
+                                             tile_off, 0, 0);
+  }
+}
+
+// Per-lane source offsets of issue_tile: LDS chunk p = (4 i + w) * 64 + lane
+// holds tile row p / DCH, global chunk (p % DCH) ^ swz(row).
+template <int D>
+__device__ __forceinline__ void tile_src_offsets(uint32_t* src_off, int wave, int lane) {
+  using T = Tile<D>;
+#pragma unroll
+  for (int i = 0; i < T::LOADS; ++i) {
+    const int p = (4 * i + wave) * 64 + lane;
+    const int row = p / T::DCH;
+    const int chunk = (p % T::DCH) ^ T::swz(row);
+    src_off[i] = (uint32_t)(row * D + chunk * 8) * 2u;
+  }
+}
+
+// Row-wise MFMA operand read from a swizzled tile: row `row`, 8 values starting
+// at column 16 ks + 8 hi (A operand of a 32x32x16 product, k = columns).
+template <int D>
+__device__ __forceinline__ bf16x8 read_rows(const TA_LDS uint16_t* t, int row, int ks, int hi,
+                                            int rswz) {
+  return *reinterpret_cast<const TA_LDS bf16x8*>(t + row * D + (((2 * ks + hi) ^ rswz) << 3));
+}
+
+// Transposed MFMA operand from a swizzled tile: the 32 columns [32 db, +32) of
+// tile rows 16 g + [0, 16) (A operand of a 32x32x16 product whose k runs over
+// tile rows).  Two LDS transpose reads (ds_read_b64_tr_b16); each 16-lane group
+// receives a 16 (columns) x 4 (rows) block.  Element e of lane l corresponds to
+// tile row 16 g + 8 (e / 4) + 4 (l / 32) + e % 4, matching the rows a 32x32
+// accumulator block holds in elements 8 (g % 2) + e.
+template <int D>
+__device__ __forceinline__ bf16x8 read_cols(const TA_LDS uint16_t* t, int g, int db, int row_lo,
+                                            int col_lo) {
+  s16x4 part[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int row = 16 * g + 8 * r + row_lo;
+    const int col = 32 * db + col_lo;
+    const int off = row * D + ((((col >> 3) ^ Tile<D>::swz(row)) << 3) | (col & 7));
+    part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TA_LDS s16x4*)(t + off));
+  }
+  return __builtin_bit_cast(bf16x8,
+                            __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+}  // namespace tiledattn

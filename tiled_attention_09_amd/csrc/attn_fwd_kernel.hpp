@@ -41,111 +41,9 @@
 //    applied only on tiles that cross the diagonal or the end of the sequence.
 #pragma once
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
-
-#include <utility>
+#include "attn_common.hpp"
 
 namespace tiledattn {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kWave = 64;
-constexpr int kWaves = 4;
-constexpr int kThreads = kWave * kWaves;
-constexpr int kBM = 128;          // query rows per workgroup (32 per wave)
-constexpr int kBN = 64;           // keys per LDS tile
-constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
-constexpr float kLn2 = 0.69314718055994530942f;
-
-#define TA_LDS __attribute__((address_space(3)))
-
-template <int D>
-struct Tile {
-  static_assert(D == 64 || D == 128, "head dim");
-  static constexpr int KS = D / 16;                 // MFMA k-steps over d for S^T
-  static constexpr int DB = D / 32;                 // 32-row blocks of O^T
-  static constexpr int DCH = D / 8;                 // 16-byte chunks per key row
-  static constexpr int BYTES = kBN * D * 2;         // one K or V tile
-  static constexpr int LOADS = BYTES / (kThreads * 16);   // 16-byte loads per thread per tile
-  static_assert(LOADS * kThreads * 16 == BYTES, "tile split");
-
-  // XOR applied to the chunk index of key row r.  d=128 (16 chunks): bijective
-  // on any 16 aligned rows, and rows 4a..4a+3 get 4 different 64-byte groups.
-  // d=64 (8 chunks, two rows per 256-byte bank window): bijective on the rows
-  // of one parity within 16 rows, and rows 4a, 4a+2 (and 4a+1, 4a+3) get
-  // different 64-byte groups.
-  __device__ static __forceinline__ int swz(int r) {
-    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-  }
-};
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
-}
-
-__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
-}
-
-// Both halves of a wave hold partial results for the same 32 queries; the
-// swap (v_permlane32_swap) gives every lane the other half's value without a
-// trip through LDS.
-__device__ __forceinline__ float other_half(float x) {
-  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false,
-                                                   false);
-  // lanes 0-31: pr[1] holds lanes 32-63; lanes 32-63: pr[0] holds lanes 0-31
-  return __int_as_float((threadIdx.x & 32) ? pr[0] : pr[1]);
-}
-
-// Issue-order recipe for the Q K^T block (group sizes must be compile-time
-// constants, hence the expansion over an index sequence): four operand reads
-// first, then alternately one MFMA and one read, the last four MFMAs at the end.
-constexpr int kSgMfma = 0x008;
-constexpr int kSgDsRead = 0x100;
-template <int KS, int... I>
-__device__ __forceinline__ void sched_qk(std::integer_sequence<int, I...>) {
-  __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4, 0);
-  ((__builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0),
-    __builtin_amdgcn_sched_group_barrier(kSgDsRead, I < 2 * KS - 4 ? 1 : 0, 0)), ...);
-}
-
-// Workgroup -> (head, query tile).  Workgroups are handed to the 8 XCDs
-// round-robin, so block b runs on XCD b % 8; consecutive logical indices are
-// given to the same XCD so one head's query tiles share that XCD's L2.
-// Causal: within a head the longest (last) query tiles go first.
-__device__ __forceinline__ void map_block(int bid, int bh_count, int n_qt, bool causal,
-                                          int& bh, int& qt) {
-  const int total = bh_count * n_qt;
-  int j = bid;
-  if ((total & 7) == 0) j = (bid & 7) * (total >> 3) + (bid >> 3);
-  bh = j / n_qt;
-  const int t = j - bh * n_qt;
-  qt = causal ? n_qt - 1 - t : t;
-}
-
-// Enqueue the copy of key tile j (K and V) into one LDS stage.  Load i of
-// wave w fills bytes [(4 i + w) * 1024, +1024) of the stage's tile, one 16-byte
-// chunk per lane; src_off holds each lane's offset within a tile.
-template <int D>
-__device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
-                                           const uint32_t* src_off, int j, int wave,
-                                           TA_LDS uint16_t* kd, TA_LDS uint16_t* vd) {
-  const uint32_t tile_off = (uint32_t)j * (uint32_t)Tile<D>::BYTES;   // scalar
-#pragma unroll
-  for (int i = 0; i < Tile<D>::LOADS; ++i) {
-    const int dst = (4 * i + wave) * 512;   // uint16 elements, wave-uniform
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (TA_LDS void*)(kd + dst), 16, src_off[i],
-                                             tile_off, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (TA_LDS void*)(vd + dst), 16, src_off[i],
-                                             tile_off, 0, 0);
-  }
-}
 
 template <int D, bool CAUSAL, bool POS_SCALE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
@@ -182,17 +80,9 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   for (int ks = 0; ks < T::KS; ++ks)
     qf[ks] = __builtin_bit_cast(bf16x8, load16(qr, (uint32_t)(my_q * D + 16 * ks + 8 * hi) * 2u));
 
-  // Tile copy offsets: LDS chunk p = (4 i + w) * 64 + lane holds key row
-  // p / DCH, global chunk (p % DCH) ^ swz(row).  They are the same for every
-  // tile and for K and V.
+  // Tile copy offsets: the same for every tile and for K and V.
   uint32_t src_off[T::LOADS];
-#pragma unroll
-  for (int i = 0; i < T::LOADS; ++i) {
-    const int p = (4 * i + wave) * 64 + lane;
-    const int row = p / T::DCH;
-    const int chunk = (p % T::DCH) ^ T::swz(row);
-    src_off[i] = (uint32_t)(row * D + chunk * 8) * 2u;
-  }
+  tile_src_offsets<D>(src_off, wave, lane);
   // Per-lane LDS byte offsets of the operand reads (tile-relative).
   // K (A operand of S^T): row kb*32 + l32, chunk (2 ks + hi) ^ swz(l32).
   const int kswz = T::swz(l32);
@@ -231,9 +121,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     for (int ks = 0; ks < T::KS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int row = kb * 32 + l32;
-        const bf16x8 a = *reinterpret_cast<const TA_LDS bf16x8*>(
-            kt + row * D + (((2 * ks + hi) ^ kswz) << 3));
+        const bf16x8 a = read_rows<D>(kt, kb * 32 + l32, ks, hi, kswz);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
       }
     // Issue order: the K operands of four MFMAs ahead, then one MFMA per read,
@@ -304,17 +192,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     for (int g = 0; g < 4; ++g)
 #pragma unroll
       for (int db = 0; db < T::DB; ++db) {
-        s16x4 part[2];
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const int key = 16 * g + 8 * r + vkey_lo;
-          const int d = 32 * db + vd_lo;
-          const int off = key * D + ((((d >> 3) ^ T::swz(key)) << 3) | (d & 7));
-          part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (TA_LDS s16x4*)(vt + off));
-        }
-        const bf16x8 a = __builtin_bit_cast(
-            bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 a = read_cols<D>(vt, g, db, vkey_lo, vd_lo);
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[g], oacc[db], 0, 0, 0);
       }
   };

@@ -9,7 +9,9 @@ seed draws standard-normal float32 tensors of shape [B, H, N, d] in the order
 Q, K, V; Q and K are multiplied by ``qk_mult`` (a power of two, so the
 multiplication is exact); all three are rounded to bfloat16 with
 round-to-nearest-even.  Sampled query rows use a second generator seeded with
-``seed + 100``.
+``seed + 100``.  The output gradient G of the backward is a standard-normal
+[B, H, N, d] tensor from a generator seeded with ``seed + 200``, rounded to
+bfloat16 the same way.
 """
 from __future__ import annotations
 
@@ -19,7 +21,8 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_qkv", "sample_rows", "bf16_bits", "headline"]
+__all__ = ["Workload", "WORKLOADS", "make_qkv", "make_dout", "sample_rows", "bf16_bits",
+           "headline"]
 
 
 @dataclass(frozen=True)
@@ -43,6 +46,12 @@ class Workload:
         """Algorithmic flops: 4*B*H*N^2*d, halved when causal."""
         f = 4.0 * self.B * self.H * self.N * self.N * self.d
         return f / 2 if self.causal else f
+
+    @property
+    def bwd_flops(self) -> float:
+        """Algorithmic backward flops: five products of 2*N^2*d each (dV, dP, dQ,
+        dK and the recomputed scores), 10*B*H*N^2*d, halved when causal."""
+        return 2.5 * self.flops
 
     @property
     def alg_bytes(self) -> int:
@@ -86,6 +95,13 @@ def make_qkv(B: int, H: int, N: int, d: int, seed: int, qk_mult: float = 1.0):
 
 def make_workload(w: Workload):
     return make_qkv(w.B, w.H, w.N, w.d, w.seed, w.qk_mult)
+
+
+def make_dout(B: int, H: int, N: int, d: int, seed: int) -> torch.Tensor:
+    """The output gradient G: contiguous CPU bfloat16 [B, H, N, d]."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed) + 200)
+    return torch.randn((B, H, N, d), generator=g, dtype=torch.float32).to(torch.bfloat16).contiguous()
 
 
 def sample_rows(N: int, count: int, seed: int) -> np.ndarray:
