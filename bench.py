@@ -1,7 +1,7 @@
 """Benchmark: fused attention forward TFLOP/s on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline]
-                    [--no-cpu-baseline]
+                    [--no-cpu-baseline] [--no-backward]
 
 A step is one attention forward over the whole workload (B=2, H=32, N=8192,
 d=128, causal, Q and K scaled by 4 -- the headline case) with inputs already
@@ -12,7 +12,11 @@ the algorithmic count 4*B*H*N^2*d, halved when causal (page "GPU Programming &
 Kernel Development", Self-check: fusion does not change the flop count).
 
 Prints ONE JSON line.  ``cpu_baseline`` times the float64 oracle (as it is) on
-a bounded sample of the same workload on the host cores.
+a bounded sample of the same workload on the host cores.  ``backward`` reports
+the gradient pass (attn_bwd: row statistics, dK/dV and dQ kernels) on the same
+workload and output gradient, timed the same way after the forward's timing;
+its flops are the algorithmic 2.5x of the forward's (five N^2 d products
+instead of two).
 """
 from __future__ import annotations
 
@@ -116,6 +120,46 @@ def cpu_baseline(w, budget_s: float = 15.0, rows_per_head: int = 2048):
                           heads, min(rows_per_head, w.N), dt, len(os.sched_getaffinity(0)))}
 
 
+def time_backward(w, q, k, v, o, lse, stream, steps: int, warmup: int):
+    """Time attn_bwd on the forward's O and LSE: HIP events on the launch
+    stream around `steps` calls after `warmup` untimed ones."""
+    import torch
+
+    import tiled_attention_09_amd as ta
+    from tiled_attention_09_amd.synth import make_dout
+    dev = q.device
+    g = make_dout(w.B, w.H, w.N, w.d, w.seed).to(dev)
+    ws = torch.empty(ta.attn_bwd_workspace_size(w.B, w.H, w.N), dtype=torch.uint8, device=dev)
+    grads = tuple(torch.empty_like(o) for _ in range(3))
+
+    def bstep():
+        ta.attn_bwd(q, k, v, o, lse, g, w.scale, w.causal, workspace=ws, grads=grads,
+                    stream=stream.cuda_stream)
+
+    for _ in range(warmup):
+        bstep()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        bstep()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ms = ev0.elapsed_time(ev1) / steps
+    achieved = w.bwd_flops / (ms * 1e-3) / 1e12
+    return {"metric": "attention bwd TFLOP/s (dQ, dK, dV; 2.5x forward flops)",
+            "value": round(w.bwd_flops / (wall_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(wall_ms, 5), "kernel_ms": round(ms, 5),
+            "flops_per_step": w.bwd_flops,
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+            "steps": steps, "warmup": warmup, "grad_dtype": "fp32", "dout_dtype": "bf16"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -123,6 +167,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--counter-pass", action="store_true",
                     help="run the calibration copy and a few launches for rocprofv3 --pmc")
     args = ap.parse_args()
@@ -215,6 +260,8 @@ def main():
         "flops_per_step": w.flops,
         "alg_bytes_per_step": w.alg_bytes,
     }
+    if not args.no_backward:
+        out["backward"] = time_backward(w, q, k, v, o, lse, stream, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
