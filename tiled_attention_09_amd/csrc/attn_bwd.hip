@@ -32,9 +32,9 @@ int launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float*
   attn_bwd_prep_kernel<D><<<dim3(prep_blocks), dim3(256), 0, stream>>>(o, g, lse, stats, N,
                                                                        stride, rows);
   attn_bwd_dkdv_kernel<D, CAUSAL><<<dim3((unsigned)(bh * n_t)), dim3(kThreads), 0, stream>>>(
-      q, k, v, g, stats, dk, dv, bh, N, stride, n_t, c, scale);
+      q, k, v, g, stats, dk, dv, bh, N, stride, n_t, c, scale, INT32_MIN);
   attn_bwd_dq_kernel<D, CAUSAL><<<dim3((unsigned)(bh * n_t)), dim3(kThreads), 0, stream>>>(
-      q, k, v, g, stats, dq, bh, N, stride, n_t, c, scale);
+      q, k, v, g, stats, dq, bh, N, stride, n_t, c, scale, INT32_MAX);
   return hipGetLastError() == hipSuccess ? TA_OK : TA_ERR_HIP;
 }
 

@@ -107,7 +107,7 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ G,
                           const f32x2* __restrict__ stats, float* __restrict__ dK,
                           float* __restrict__ dV, int bh_count, int N, int stats_stride,
-                          int n_kt, float c, float scale) {
+                          int n_kt, float c, float scale, int skip_floor) {
   using T = Tile<D>;
   __shared__ __attribute__((aligned(1024))) uint16_t q_lds0[kBN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t g_lds0[kBN * D];
@@ -147,9 +147,7 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 
   uint32_t src_off[T::LOADS];
   tile_src_offsets<D>(src_off, wave, lane);
-  const int rswz = T::swz(l32);
-  const int row_lo = 4 * hi + ((lane & 15) >> 2);              // transpose-read source row
-  const int col_lo = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // transpose-read source column
+  const LdsReader<D> rd(lane);
 
   f32x16 dk[T::DB], dv[T::DB];
 #pragma unroll
@@ -166,7 +164,7 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   auto compute_tile = [&](int i, const TA_LDS uint16_t* qt, const TA_LDS uint16_t* gt,
                           const TA_LDS float* st) {
     const int qbase = i * kBN;
-    // S and dP: 2 blocks of 32 queries x the wave's 32 keys.
+    // S and dP: 2 blocks of 32 queries x the wave's 32 keys (4 KS products).
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
@@ -179,42 +177,58 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     for (int ks = 0; ks < T::KS; ++ks)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const bf16x8 aq = read_rows<D>(qt, qb * 32 + l32, ks, hi, rswz);
+        const bf16x8 aq = rd.row_op(qt, qb, ks);
         s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ks], s[qb], 0, 0, 0);
       }
 #pragma unroll
     for (int ks = 0; ks < T::KS; ++ks)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const bf16x8 ag = read_rows<D>(gt, qb * 32 + l32, ks, hi, rswz);
+        const bf16x8 ag = rd.row_op(gt, qb, ks);
         dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, vf[ks], dp[qb], 0, 0, 0);
       }
+    // {LSE2, D} of the 16 query rows each lane holds: element 4 g4 + t of
+    // block qb is tile row 32 qb + 8 g4 + 4 hi + t.
+    f32x4 sta[8], stb[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int qrow = 32 * (r >> 2) + 8 * (r & 3) + 4 * hi;
+      sta[r] = *reinterpret_cast<const TA_LDS f32x4*>(st + 2 * qrow);
+      stb[r] = *reinterpret_cast<const TA_LDS f32x4*>(st + 2 * qrow + 4);
+    }
+    sched_mfma_ds<4, 1, 4 * T::KS + 16>(std::make_integer_sequence<int, 4 * T::KS>{});
 
-    // P = 2^(c s - LSE2) and dS = P (dP - D); element e of block qb is query
-    // qbase + 32 qb + 8 (e / 4) + 4 hi + e % 4 of key my_k.
+    // Exponent arguments c s - LSE2; hidden pairs (query before key, or query
+    // past the end) get -inf, which exp2 turns into an exact 0.
     const bool edge = (CAUSAL && qbase < k0 + 31) || (qbase + kBN > N);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = 4 * qb + (e >> 2), t = e & 3;
+        const float lse2 = (t < 2) ? sta[r][2 * t] : stb[r][2 * (t - 2)];
+        s[qb][e] = __builtin_fmaf(s[qb][e], c, -lse2);
+      }
+    if (edge) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int q = qbase + 32 * qb + 8 * (e >> 2) + 4 * hi + (e & 3);
+          if ((CAUSAL && my_k > q) || q >= N) s[qb][e] = -__builtin_inff();
+        }
+    }
+    // P = 2^arg and dS = P (dP - D), rounded to bf16 as B operands.
     bf16x8 pf[4], sf[4];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int qrow = 32 * qb + 8 * g4 + 4 * hi;          // tile row of element 4 g4
-        const f32x4 sa = *reinterpret_cast<const TA_LDS f32x4*>(st + 2 * qrow);
-        const f32x4 sb = *reinterpret_cast<const TA_LDS f32x4*>(st + 2 * qrow + 4);
-        const float lse2[4] = {sa[0], sa[2], sb[0], sb[2]};
-        const float dd[4] = {sa[1], sa[3], sb[1], sb[3]};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int e = 4 * g4 + t;
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][e], c, -lse2[t]));
-          if (edge) {
-            const int q = qbase + qrow + t;
-            if ((CAUSAL && my_k > q) || q >= N) p = 0.f;
-          }
-          const float ds = p * (dp[qb][e] - dd[t]);
-          pf[2 * qb + (e >> 3)][e & 7] = (__bf16)p;
-          sf[2 * qb + (e >> 3)][e & 7] = (__bf16)ds;
-        }
+      for (int e = 0; e < 16; ++e) {
+        const int r = 4 * qb + (e >> 2), t = e & 3;
+        const float dd = (t < 2) ? sta[r][2 * t + 1] : stb[r][2 * (t - 2) + 1];
+        const float p = __builtin_amdgcn_exp2f(s[qb][e]);
+        pf[2 * qb + (e >> 3)][e & 7] = (__bf16)p;
+        sf[2 * qb + (e >> 3)][e & 7] = (__bf16)(p * (dp[qb][e] - dd));
       }
 
     // dV^T (d x 32 keys) += G^T (d x 64 queries) P;  dK^T += Q^T dS.
@@ -222,11 +236,12 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     for (int g = 0; g < 4; ++g)
 #pragma unroll
       for (int db = 0; db < T::DB; ++db) {
-        const bf16x8 ag = read_cols<D>(gt, g, db, row_lo, col_lo);
+        const bf16x8 ag = rd.col_op(gt, g, db);
         dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, pf[g], dv[db], 0, 0, 0);
-        const bf16x8 aq = read_cols<D>(qt, g, db, row_lo, col_lo);
+        const bf16x8 aq = rd.col_op(qt, g, db);
         dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sf[g], dk[db], 0, 0, 0);
       }
+    sched_mfma_ds<8, 2, 16 * T::DB>(std::make_integer_sequence<int, 8 * T::DB>{});
   };
 
   TA_LDS uint16_t* const q0p = (TA_LDS uint16_t*)q_lds0;
@@ -236,8 +251,12 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   TA_LDS float* const s0p = (TA_LDS float*)st_lds0;
   TA_LDS float* const s1p = (TA_LDS float*)st_lds1;
   // A wave's keys are all hidden from query tile i when its last query
-  // precedes the wave's first key.
-  auto active = [&](int i) { return !(CAUSAL && i * kBN + kBN - 1 < k0); };
+  // precedes the wave's first key.  Without the causal mask the host passes
+  // INT_MIN as skip_floor: the test is then always true, but stays a runtime
+  // branch, which keeps each tile's products in a scheduling region of its own
+  // (merged regions made the compiler spill).
+  const int first_key = CAUSAL ? k0 : skip_floor;
+  auto active = [&](int i) { return i * kBN + kBN - 1 >= first_key; };
   // Each stage holds the Q and G rows of one query tile and their {LSE2, D}.
   if (i0 < n_qt) {
     issue_tile<D>(qr, gr, src_off, i0, wave, q0p, g0p);
@@ -286,7 +305,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                         const uint16_t* __restrict__ V, const uint16_t* __restrict__ G,
                         const f32x2* __restrict__ stats, float* __restrict__ dQ, int bh_count,
-                        int N, int stats_stride, int n_qt, float c, float scale) {
+                        int N, int stats_stride, int n_qt, float c, float scale,
+                        int skip_ceiling) {
   using T = Tile<D>;
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[kBN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[kBN * D];
@@ -329,9 +349,7 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 
   uint32_t src_off[T::LOADS];
   tile_src_offsets<D>(src_off, wave, lane);
-  const int rswz = T::swz(l32);
-  const int row_lo = 4 * hi + ((lane & 15) >> 2);
-  const int col_lo = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const LdsReader<D> rd(lane);
 
   f32x16 dq[T::DB];
 #pragma unroll
@@ -344,53 +362,63 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 
   auto compute_tile = [&](int j, const TA_LDS uint16_t* kt, const TA_LDS uint16_t* vt) {
     const int key0 = j * kBN;
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        s[kb][e] = 0.f;
-        dp[kb][e] = 0.f;
-      }
-#pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 ak = read_rows<D>(kt, kb * 32 + l32, ks, hi, rswz);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[ks], s[kb], 0, 0, 0);
-      }
-#pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 av = read_rows<D>(vt, kb * 32 + l32, ks, hi, rswz);
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, gf[ks], dp[kb], 0, 0, 0);
-      }
-
-    // Element e of block kb is key key0 + 32 kb + 8 (e / 4) + 4 hi + e % 4 of query my_q.
     const bool edge = (CAUSAL && key0 + kBN - 1 > q0) || (key0 + kBN > N);
-    bf16x8 sf[4];
+    // One 32-key block at a time: S^T and dP^T (32 keys x 32 queries), then
+    // its dS^T, then its share of dQ^T.
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s, dp;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e], c, -lse2));
-        if (edge) {
-          const int key = key0 + kb * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
-          if ((CAUSAL && key > my_q) || key >= N) p = 0.f;
-        }
-        sf[2 * kb + (e >> 3)][e & 7] = (__bf16)(p * (dp[kb][e] - dd));
+        s[e] = 0.f;
+        dp[e] = 0.f;
       }
+#pragma unroll
+      for (int ks = 0; ks < T::KS; ++ks) {
+        const bf16x8 ak = rd.row_op(kt, kb, ks);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[ks], s, 0, 0, 0);
+      }
+#pragma unroll
+      for (int ks = 0; ks < T::KS; ++ks) {
+        const bf16x8 av = rd.row_op(vt, kb, ks);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, gf[ks], dp, 0, 0, 0);
+      }
+      sched_mfma_ds<4, 1, 2 * T::KS>(std::make_integer_sequence<int, 2 * T::KS>{});
 
-    // dQ^T (d x 32 queries) += K^T (d x 64 keys) dS^T (64 keys x 32 queries).
+      // Element e is key key0 + 32 kb + 8 (e / 4) + 4 hi + e % 4 of query my_q;
+      // hidden keys get exponent -inf (an exact 0).
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+      for (int e = 0; e < 16; ++e) s[e] = __builtin_fmaf(s[e], c, -lse2);
+      if (edge) {
 #pragma unroll
-      for (int db = 0; db < T::DB; ++db) {
-        const bf16x8 ak = read_cols<D>(kt, g, db, row_lo, col_lo);
-        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, sf[g], dq[db], 0, 0, 0);
+        for (int e = 0; e < 16; ++e) {
+          const int key = key0 + kb * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+          if ((CAUSAL && key > my_q) || key >= N) s[e] = -__builtin_inff();
+        }
       }
+      bf16x8 sf[2];
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        sf[e >> 3][e & 7] = (__bf16)(__builtin_amdgcn_exp2f(s[e]) * (dp[e] - dd));
+
+      // dQ^T (d x 32 queries) += K^T (d x these 32 keys) dS^T.
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db) {
+          const bf16x8 ak = rd.col_op(kt, 2 * kb + h, db);
+          dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, sf[h], dq[db], 0, 0, 0);
+        }
+      sched_mfma_ds<8, 2, 4 * T::DB>(std::make_integer_sequence<int, 2 * T::DB>{});
+    }
   };
+
+  // A wave's queries all precede key tile j when its first key is past the
+  // wave's last query.  Without the causal mask the host passes INT_MAX as
+  // skip_ceiling: always true, but a runtime branch that keeps the two tiles
+  // of an iteration in separate scheduling regions.
+  const int last_query = CAUSAL ? q0 + 31 : skip_ceiling;
+  auto active = [&](int j) { return j * kBN <= last_query; };
 
   TA_LDS uint16_t* const k0p = (TA_LDS uint16_t*)k_lds0;
   TA_LDS uint16_t* const v0p = (TA_LDS uint16_t*)v_lds0;
@@ -401,12 +429,12 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (j + 1 < n_kt) issue_tile<D>(kr, vr, src_off, j + 1, wave, k1p, v1p);
-    if (!(CAUSAL && j * kBN > q0 + 31)) compute_tile(j, k0p, v0p);
+    if (active(j)) compute_tile(j, k0p, v0p);
     if (j + 1 >= n_kt) break;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (j + 2 < n_kt) issue_tile<D>(kr, vr, src_off, j + 2, wave, k0p, v0p);
-    if (!(CAUSAL && (j + 1) * kBN > q0 + 31)) compute_tile(j + 1, k1p, v1p);
+    if (active(j + 1)) compute_tile(j + 1, k1p, v1p);
   }
 
   if (my_q < N) {

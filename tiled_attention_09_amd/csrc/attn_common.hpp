@@ -84,6 +84,21 @@ __device__ __forceinline__ void sched_qk(std::integer_sequence<int, I...>) {
     __builtin_amdgcn_sched_group_barrier(kSgDsRead, I < 2 * KS - 4 ? 1 : 0, 0)), ...);
 }
 
+// Issue-order recipe for a block of NMFMA matrix products fed by LDS reads:
+// PRE reads first, then each product followed by up to PER more reads until
+// TOTAL reads are placed (group sizes must be compile-time constants, hence the
+// expansion over an index sequence).  Keeps PRE / PER products' worth of reads
+// in flight instead of waiting on each operand just before its product.
+template <int PRE, int PER, int TOTAL, int... I>
+__device__ __forceinline__ void sched_mfma_ds(std::integer_sequence<int, I...>) {
+  __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);
+  ((__builtin_amdgcn_sched_group_barrier(0x008, 1, 0),
+    __builtin_amdgcn_sched_group_barrier(
+        0x100, (TOTAL - PRE - PER * I) >= PER ? PER : ((TOTAL - PRE - PER * I) > 0 ? (TOTAL - PRE - PER * I) : 0),
+        0)),
+   ...);
+}
+
 // Workgroup -> (head, row tile).  Workgroups are handed to the 8 XCDs
 // round-robin, so block b runs on XCD b % 8; consecutive logical indices are
 // given to the same XCD so one head's tiles share that XCD's L2.  With
@@ -160,5 +175,50 @@ __device__ __forceinline__ bf16x8 read_cols(const TA_LDS uint16_t* t, int g, int
   return __builtin_bit_cast(bf16x8,
                             __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
 }
+
+// The same two reads with the addresses split so that only a per-lane XOR with
+// a compile-time constant remains: a row's 16-byte chunk index sits in byte
+// bits 4.. (below the row bits), the swizzle only mixes chunk bits, and every
+// term that varies by whole rows (the 32-row block, the 16-row group g, the
+// LDS stage) is a constant the compiler folds into the ds_read offset field.
+// This keeps the lane-dependent address registers to KS + 2 DB instead of one
+// per (stage, row block, k-step).
+template <int D>
+struct LdsReader {
+  uint32_t rows;      // byte offset of (row l32, chunk hi ^ swz(l32)) in a tile
+  uint32_t cols[2];   // byte offset of the transpose-read source for r = 0, 1
+
+  __device__ __forceinline__ LdsReader(int lane) {
+    const int l32 = lane & 31, hi = lane >> 5;
+    rows = (uint32_t)(l32 * D * 2) | ((uint32_t)(hi ^ Tile<D>::swz(l32)) << 4);
+    const int row_lo = 4 * hi + ((lane & 15) >> 2);               // source row within 8
+    const int col_lo = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);   // source column within 32
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int row = 8 * r + row_lo;
+      cols[r] = (uint32_t)(row * D * 2) |
+                ((uint32_t)((col_lo >> 3) ^ Tile<D>::swz(row)) << 4) | (uint32_t)((col_lo & 7) * 2);
+    }
+  }
+
+  // A operand from rows 32 rb + l32, columns 16 ks + 8 hi + [0, 8).
+  __device__ __forceinline__ bf16x8 row_op(const TA_LDS uint16_t* t, int rb, int ks) const {
+    const uint32_t off = (uint32_t)(rb * 32 * D * 2) + (rows ^ (uint32_t)(ks << 5));
+    return *reinterpret_cast<const TA_LDS bf16x8*>((const TA_LDS char*)t + off);
+  }
+
+  // Transposed A operand: columns [32 db, +32) of rows 16 g + [0, 16).
+  __device__ __forceinline__ bf16x8 col_op(const TA_LDS uint16_t* t, int g, int db) const {
+    s16x4 part[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const uint32_t off = (uint32_t)(g * 16 * D * 2) + (cols[r] ^ (uint32_t)(db << 6));
+      part[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (TA_LDS s16x4*)((const TA_LDS char*)t + off));
+    }
+    return __builtin_bit_cast(bf16x8,
+                              __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+};
 
 }  // namespace tiledattn
