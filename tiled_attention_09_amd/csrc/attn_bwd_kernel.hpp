@@ -164,15 +164,32 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   auto compute_tile = [&](int i, const TA_LDS uint16_t* qt, const TA_LDS uint16_t* gt,
                           const TA_LDS float* st) {
     const int qbase = i * kBN;
-    // S and dP: 2 blocks of 32 queries x the wave's 32 keys (4 KS products).
+    // Row statistics of the 16 query rows each lane holds per block: element
+    // 4 g4 + t of block qb is tile row 32 qb + 8 g4 + 4 hi + t.  LSE2 is kept
+    // for the exponent; -D is the starting value of the dP accumulator, so the
+    // products below yield dP - D directly.
     f32x16 s[2], dp[2];
+    float lse2[2][16];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int qb = r >> 2, g4 = r & 3;
+      const int qrow = 32 * qb + 8 * g4 + 4 * hi;
+      const f32x4 a = *reinterpret_cast<const TA_LDS f32x4*>(st + 2 * qrow);
+      const f32x4 b = *reinterpret_cast<const TA_LDS f32x4*>(st + 2 * qrow + 4);
+      lse2[qb][4 * g4 + 0] = a[0];
+      lse2[qb][4 * g4 + 1] = a[2];
+      lse2[qb][4 * g4 + 2] = b[0];
+      lse2[qb][4 * g4 + 3] = b[2];
+      dp[qb][4 * g4 + 0] = -a[1];
+      dp[qb][4 * g4 + 1] = -a[3];
+      dp[qb][4 * g4 + 2] = -b[1];
+      dp[qb][4 * g4 + 3] = -b[3];
+    }
+    // S and dP - D: 2 blocks of 32 queries x the wave's 32 keys (4 KS products).
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        s[qb][e] = 0.f;
-        dp[qb][e] = 0.f;
-      }
+      for (int e = 0; e < 16; ++e) s[qb][e] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < T::KS; ++ks)
 #pragma unroll
@@ -187,16 +204,7 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         const bf16x8 ag = rd.row_op(gt, qb, ks);
         dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, vf[ks], dp[qb], 0, 0, 0);
       }
-    // {LSE2, D} of the 16 query rows each lane holds: element 4 g4 + t of
-    // block qb is tile row 32 qb + 8 g4 + 4 hi + t.
-    f32x4 sta[8], stb[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int qrow = 32 * (r >> 2) + 8 * (r & 3) + 4 * hi;
-      sta[r] = *reinterpret_cast<const TA_LDS f32x4*>(st + 2 * qrow);
-      stb[r] = *reinterpret_cast<const TA_LDS f32x4*>(st + 2 * qrow + 4);
-    }
-    sched_mfma_ds<4, 1, 4 * T::KS + 16>(std::make_integer_sequence<int, 4 * T::KS>{});
+    sched_mfma_ds<20, 1, 4 * T::KS + 16>(std::make_integer_sequence<int, 4 * T::KS>{});
 
     // Exponent arguments c s - LSE2; hidden pairs (query before key, or query
     // past the end) get -inf, which exp2 turns into an exact 0.
@@ -204,11 +212,7 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int r = 4 * qb + (e >> 2), t = e & 3;
-        const float lse2 = (t < 2) ? sta[r][2 * t] : stb[r][2 * (t - 2)];
-        s[qb][e] = __builtin_fmaf(s[qb][e], c, -lse2);
-      }
+      for (int e = 0; e < 16; ++e) s[qb][e] = __builtin_fmaf(s[qb][e], c, -lse2[qb][e]);
     if (edge) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
@@ -224,11 +228,9 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int r = 4 * qb + (e >> 2), t = e & 3;
-        const float dd = (t < 2) ? sta[r][2 * t + 1] : stb[r][2 * (t - 2) + 1];
         const float p = __builtin_amdgcn_exp2f(s[qb][e]);
         pf[2 * qb + (e >> 3)][e & 7] = (__bf16)p;
-        sf[2 * qb + (e >> 3)][e & 7] = (__bf16)(p * (dp[qb][e] - dd));
+        sf[2 * qb + (e >> 3)][e & 7] = (__bf16)(p * dp[qb][e]);
       }
 
     // dV^T (d x 32 keys) += G^T (d x 64 queries) P;  dK^T += Q^T dS.
@@ -258,19 +260,19 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   const int first_key = CAUSAL ? k0 : skip_floor;
   auto active = [&](int i) { return i * kBN + kBN - 1 >= first_key; };
   // Each stage holds the Q and G rows of one query tile and their {LSE2, D}.
+  // Pairs of tiles run in the loop (stage 0, stage 1); an odd last tile runs
+  // after it, so the loop has a single exit.
   if (i0 < n_qt) {
     issue_tile<D>(qr, gr, src_off, i0, wave, q0p, g0p);
     issue_stats(sr, i0, wave, lane, s0p);
   }
-  for (int i = i0; i < n_qt; i += 2) {
+  int i = i0;
+  for (; i + 1 < n_qt; i += 2) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();                       // tile i visible; tile i-1's readers done
-    if (i + 1 < n_qt) {
-      issue_tile<D>(qr, gr, src_off, i + 1, wave, q1p, g1p);
-      issue_stats(sr, i + 1, wave, lane, s1p);
-    }
+    issue_tile<D>(qr, gr, src_off, i + 1, wave, q1p, g1p);
+    issue_stats(sr, i + 1, wave, lane, s1p);
     if (active(i)) compute_tile(i, q0p, g0p, s0p);
-    if (i + 1 >= n_qt) break;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (i + 2 < n_qt) {
@@ -278,6 +280,11 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
       issue_stats(sr, i + 2, wave, lane, s0p);
     }
     if (active(i + 1)) compute_tile(i + 1, q1p, g1p, s1p);
+  }
+  if (i < n_qt) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (active(i)) compute_tile(i, q0p, g0p, s0p);
   }
 
   // Epilogue: lane owns key my_k; accumulator element e of block db is column
