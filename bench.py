@@ -37,51 +37,61 @@ COPY_BYTES = 256 << 20           # calibration copy of --counter-pass (bytes rea
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_headline_traffic.json")
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the HIP sources of the library (traffic figures are only
-    valid for the kernel they were measured on)."""
+FWD_SOURCES = ("attn_common.hpp", "attn_fwd.hip", "attn_fwd_kernel.hpp")
+BWD_SOURCES = ("attn_bwd.hip", "attn_bwd_kernel.hpp", "attn_common.hpp")
+BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bwd_headline_traffic.json")
+
+
+def kernel_source_hash(names=FWD_SOURCES) -> str:
+    """sha256 over the HIP sources a kernel is built from (traffic figures are
+    only valid for the kernel they were measured on)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tiled_attention_09_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(names):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload_name: str):
-    """HBM bytes per launch from the committed counter summary, or None when it
+def measured_traffic(workload_name: str, path: str = TRAFFIC_FILE, names=FWD_SOURCES):
+    """HBM bytes per launch from a committed counter summary, or None when it
     is missing, for another workload, or older than the current kernel."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return None
-    t = json.load(open(TRAFFIC_FILE))
-    if t.get("workload") != workload_name or t.get("kernel_source_sha256") != kernel_source_hash():
+    t = json.load(open(path))
+    if t.get("workload") != workload_name or t.get("kernel_source_sha256") != kernel_source_hash(names):
         return None
     return t.get("bytes_per_launch")
 
 
 def counter_pass(w, launches: int = 3):
     """For rocprofv3 --pmc runs: one plain device copy of COPY_BYTES (the
-    calibration dispatch), then `launches` attention launches."""
+    calibration dispatch), then `launches` forward launches and `launches`
+    backward calls (each: row statistics, dK/dV, dQ kernels)."""
     import torch
 
     import tiled_attention_09_amd as ta
-    from tiled_attention_09_amd.synth import make_workload
+    from tiled_attention_09_amd.synth import make_dout, make_workload
     dev = torch.device("cuda:0")
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     q, k, v = (x.to(dev) for x in make_workload(w))
+    g = make_dout(w.B, w.H, w.N, w.d, w.seed).to(dev)
     torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
     for _ in range(launches):
-        ta.attn_fwd(q, k, v, w.scale, w.causal)
+        o, lse = ta.attn_fwd(q, k, v, w.scale, w.causal)
     torch.cuda.synchronize()
-    print("counter pass: 1 copy of %d bytes, %d attention launches (%s)" % (
-        COPY_BYTES, launches, w.describe()), flush=True)
+    for _ in range(launches):
+        ta.attn_bwd(q, k, v, o, lse, g, w.scale, w.causal)
+    torch.cuda.synchronize()
+    print("counter pass: 1 copy of %d bytes, %d forward and %d backward launches (%s)" % (
+        COPY_BYTES, launches, launches, w.describe()), flush=True)
 
 
-def cpu_baseline(w, budget_s: float = 15.0, rows_per_head: int = 2048):
+def cpu_baseline(w, budget_s: float = 15.0, rows_per_head: int = 4096):
     """Time the float64 oracle on a seeded row sample of every head, head by
     head, until the time budget is spent.  Returns the JSON object."""
     import numpy as np
@@ -156,7 +166,8 @@ def time_backward(w, q, k, v, o, lse, stream, steps: int, warmup: int):
             "flops_per_step": w.bwd_flops,
             "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                         "traffic": measured_traffic(w.name, BWD_TRAFFIC_FILE, BWD_SOURCES)},
             "steps": steps, "warmup": warmup, "grad_dtype": "fp32", "dout_dtype": "bf16"}
 
 

@@ -115,7 +115,7 @@ __device__ __forceinline__ void map_block(int bid, int bh_count, int n_t, bool r
 }
 
 // Enqueue the copy of row tile j of two matrices (K and V; Q and dO) into one
-// LDS stage.  Load i of wave w fills bytes [(4 i + w) * 1024, +1024) of the
+// LDS stage.  Load i of wave w fills bytes [(W i + w) * 1024, +1024) (W waves) of the
 // stage's tile, one 16-byte chunk per lane; src_off holds each lane's offset
 // within a tile (tile_src_offsets).
 template <int D>
@@ -125,7 +125,7 @@ __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t kr, __amdgpu_b
   const uint32_t tile_off = (uint32_t)j * (uint32_t)Tile<D>::BYTES;   // scalar
 #pragma unroll
   for (int i = 0; i < Tile<D>::LOADS; ++i) {
-    const int dst = (4 * i + wave) * 512;   // uint16 elements, wave-uniform
+    const int dst = (kWaves * i + wave) * 512;   // uint16 elements, wave-uniform
     __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (TA_LDS void*)(kd + dst), 16, src_off[i],
                                              tile_off, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (TA_LDS void*)(vd + dst), 16, src_off[i],
@@ -133,14 +133,14 @@ __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t kr, __amdgpu_b
   }
 }
 
-// Per-lane source offsets of issue_tile: LDS chunk p = (4 i + w) * 64 + lane
+// Per-lane source offsets of issue_tile: LDS chunk p = (W i + w) * 64 + lane
 // holds tile row p / DCH, global chunk (p % DCH) ^ swz(row).
 template <int D>
 __device__ __forceinline__ void tile_src_offsets(uint32_t* src_off, int wave, int lane) {
   using T = Tile<D>;
 #pragma unroll
   for (int i = 0; i < T::LOADS; ++i) {
-    const int p = (4 * i + wave) * 64 + lane;
+    const int p = (kWaves * i + wave) * 64 + lane;
     const int row = p / T::DCH;
     const int chunk = (p % T::DCH) ^ T::swz(row);
     src_off[i] = (uint32_t)(row * D + chunk * 8) * 2u;

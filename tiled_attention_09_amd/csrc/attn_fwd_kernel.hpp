@@ -83,14 +83,9 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   // Tile copy offsets: the same for every tile and for K and V.
   uint32_t src_off[T::LOADS];
   tile_src_offsets<D>(src_off, wave, lane);
-  // Per-lane LDS byte offsets of the operand reads (tile-relative).
-  // K (A operand of S^T): row kb*32 + l32, chunk (2 ks + hi) ^ swz(l32).
-  const int kswz = T::swz(l32);
-  // V (A operand of O^T via transpose read): for read r of key group g and
-  // d block db, source lane reads 4 d-values at key 16 g + 8 r + 4 hi + (lane%16)/4,
-  // d = 32 db + 16 ((lane >> 4) & 1) + 4 (lane & 3).
-  const int vkey_lo = 4 * hi + ((lane & 15) >> 2);                 // key within an 8-key slice
-  const int vd_lo = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);       // d within a 32-d block
+  // Operand reads: K row-wise (A operand of S^T), V transposed (A operand of
+  // O^T), with lane offsets whose row/stage parts fold into the instruction.
+  const LdsReader<D> rd(lane);
 
   f32x16 oacc[T::DB];
 #pragma unroll
@@ -121,7 +116,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     for (int ks = 0; ks < T::KS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = read_rows<D>(kt, kb * 32 + l32, ks, hi, kswz);
+        const bf16x8 a = rd.row_op(kt, kb, ks);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
       }
     // Issue order: the K operands of four MFMAs ahead, then one MFMA per read,
@@ -192,7 +187,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     for (int g = 0; g < 4; ++g)
 #pragma unroll
       for (int db = 0; db < T::DB; ++db) {
-        const bf16x8 a = read_cols<D>(vt, g, db, vkey_lo, vd_lo);
+        const bf16x8 a = rd.col_op(vt, g, db);
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[g], oacc[db], 0, 0, 0);
       }
   };
