@@ -171,6 +171,66 @@ def time_backward(w, q, k, v, o, lse, stream, steps: int, warmup: int):
             "steps": steps, "warmup": warmup, "grad_dtype": "fp32", "dout_dtype": "bf16"}
 
 
+# General-shape forward workloads (attn_fwd_ex): name, B, H, Nq, Nk, d, dv, offset, causal.
+GENERAL = [
+    ("chunked prefill: 1024 queries at positions 7168.. of 8192 keys", 2, 32, 1024, 8192, 128, 128,
+     7168, True),
+    ("value width 64: B=2,H=32,N=8192,d=128,dv=64", 2, 32, 8192, 8192, 128, 64, 0, True),
+    ("decode step: 1 query at position 8191 of 8192 keys, B=16,H=32", 16, 32, 1, 8192, 128, 128,
+     8191, True),
+]
+
+
+def time_general(stream, steps: int, warmup: int):
+    """Time attn_fwd_ex on the GENERAL workloads (seeded bf16 normal inputs).
+    Flops count the visible (query, key) pairs: 2 (d + dv) per pair; bytes are
+    Q, K, V read once and O, LSE written once."""
+    import torch
+
+    import tiled_attention_09_amd as ta
+    dev = torch.device("cuda:0")
+    res = []
+    for (name, B, H, Nq, Nk, d, dv, off, causal) in GENERAL:
+        g = torch.Generator(device="cpu")
+        g.manual_seed(900 + Nq)
+        q = torch.randn((B, H, Nq, d), generator=g).to(torch.bfloat16).to(dev)
+        k = torch.randn((B, H, Nk, d), generator=g).to(torch.bfloat16).to(dev)
+        v = torch.randn((B, H, Nk, dv), generator=g).to(torch.bfloat16).to(dev)
+        o = torch.empty((B, H, Nq, dv), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+
+        def run():
+            ta.attn_fwd_ex(q, k, v, 1.0 / d ** 0.5, causal, off, out=o, lse=lse,
+                           stream=stream.cuda_stream)
+
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        pairs = sum(min(Nk, off + i + 1) for i in range(Nq)) if causal else Nq * Nk
+        flops = 2.0 * (d + dv) * B * H * pairs
+        nbytes = B * H * (Nq * d * 2 + Nk * (d + dv) * 2 + Nq * dv * 4 + Nq * 4)
+        tflops = flops / (ms * 1e-3) / 1e12
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        hbm_bound = flops / nbytes < (PEAK_BF16_TFLOPS * 1e12) / (PEAK_HBM_GBS * 1e9)
+        roof = ({"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                 "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None} if hbm_bound else
+                {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                 "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None})
+        res.append({"workload": name, "B": B, "H": H, "Nq": Nq, "Nk": Nk, "d": d, "dv": dv,
+                    "query_offset": off, "causal": causal, "kernel_ms": round(ms, 5),
+                    "tflops": round(tflops, 2), "gbs": round(gbs, 1), "flops": flops,
+                    "alg_bytes": nbytes, "roofline": roof, "steps": steps})
+        del q, k, v, o, lse
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -179,6 +239,7 @@ def main():
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-general", action="store_true")
     ap.add_argument("--counter-pass", action="store_true",
                     help="run the calibration copy and a few launches for rocprofv3 --pmc")
     args = ap.parse_args()
@@ -273,6 +334,10 @@ def main():
     }
     if not args.no_backward:
         out["backward"] = time_backward(w, q, k, v, o, lse, stream, args.steps, args.warmup)
+    if not args.no_general:
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+        out["general_shapes"] = time_general(stream, max(5, args.steps // 2), max(2, args.warmup // 2))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

@@ -32,7 +32,7 @@ extern "C" {
 /* Status codes returned by every entry point. */
 typedef enum {
   TA_OK = 0,              /* enqueued (or nothing to do)                          */
-  TA_ERR_INVALID_ARG = 1, /* a size, flag, pointer or scale is out of range       */
+  TA_ERR_INVALID_ARG = 1, /* a size, offset, flag, pointer or scale is out of range */
   TA_ERR_UNSUPPORTED = 2, /* head dimension other than 64 or 128                  */
   TA_ERR_MISALIGNED = 3,  /* q, k, v or o not 16-byte aligned, lse not 4-byte     */
   TA_ERR_HIP = 4          /* the HIP runtime reported an error at launch          */
@@ -69,6 +69,34 @@ typedef enum {
  */
 int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
              int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * attn_fwd_ex -- attn_fwd for general shapes: Nq queries attending Nk keys,
+ * value width dv, and queries placed at absolute positions query_offset ..
+ * query_offset + Nq - 1 (the decoding-style subproblems of the lab on page
+ * "22. GPU Engineering: Correctness, Throughput, and Attention", sec. 22.7:
+ * a nonnegative query-position offset, the causal rule on absolute
+ * positions, and the policy for rows that see no key).
+ *
+ *     S[i,j] = scale * <q_i, k_j>     hidden when causal and j > i + query_offset
+ *     O[i,:] = sum_j softmax_j(S[i,:]) v_j,   LSE[i] = ln sum_j exp(S[i,j])
+ *     a row with no visible key (only possible when Nk = 0): O[i,:] = 0, LSE[i] = -inf
+ *
+ *   q   : device bf16 [B, H, Nq, d];  k: device bf16 [B, H, Nk, d];
+ *   v   : device bf16 [B, H, Nk, dv]; read only, contiguous, rows of a head consecutive.
+ *   o   : device fp32 [B, H, Nq, dv], written;  lse: device fp32 [B, H, Nq], written.
+ *   Nq, Nk       : 0 .. 2^22 each (Nq = 0: nothing is enqueued, TA_OK).  q, o and
+ *                  lse may be NULL when Nq = 0, k and v when Nk = 0.
+ *   d, dv        : 64 or 128 each (TA_ERR_UNSUPPORTED otherwise).
+ *   query_offset : 0 .. 2^30 (the lab requires it nonnegative); ignored when causal = 0.
+ *   B, H, scale, causal, stream, ownership, alignment and errors: as for attn_fwd.
+ *
+ * attn_fwd(q, k, v, o, lse, B, H, N, d, ...) computes exactly
+ * attn_fwd_ex(q, k, v, o, lse, B, H, N, N, d, d, 0, ...).
+ */
+int attn_fwd_ex(const void* q, const void* k, const void* v, float* o, float* lse,
+                int B, int H, int Nq, int Nk, int d, int dv, int query_offset,
+                float scale, int causal, void* stream);
 
 /*
  * attn_bwd_workspace_size -- bytes of device workspace attn_bwd needs for

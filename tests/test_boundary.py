@@ -41,7 +41,7 @@ def declared_functions():
 
 def test_header_declares_entry_points():
     assert declared_functions() == ["attn_bwd", "attn_bwd_workspace_size", "attn_fwd",
-                                    "attn_status_string"]
+                                    "attn_fwd_ex", "attn_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -164,3 +164,58 @@ def test_python_bwd_wrapper_rejects_cpu_tensors():
     o = torch.zeros(1, 1, 8, 64)
     with pytest.raises(ValueError):
         ta.attn_bwd(x, x, x, o, torch.zeros(1, 1, 8), x)
+
+
+# ---- general-shape forward ---------------------------------------------------
+
+def call_ex(**over):
+    args = dict(q=A, k=A, v=A, o=A, lse=A, B=1, H=1, Nq=16, Nk=128, d=64, dv=128, off=112,
+                scale=0.125, causal=1)
+    args.update(over)
+    return ta.attn_fwd_ex_raw(args["q"], args["k"], args["v"], args["o"], args["lse"], args["B"],
+                              args["H"], args["Nq"], args["Nk"], args["d"], args["dv"], args["off"],
+                              args["scale"], args["causal"], 0)
+
+
+@host_only
+@pytest.mark.parametrize("field", ["q", "k", "v", "o", "lse"])
+def test_ex_null_pointer(field):
+    assert call_ex(**{field: 0}) == ta.TA_ERR_INVALID_ARG
+
+
+@host_only
+@pytest.mark.parametrize("over", [dict(off=-1), dict(off=(1 << 30) + 1), dict(Nq=-1), dict(Nk=-1),
+                                  dict(Nq=(1 << 22) + 1), dict(Nk=(1 << 22) + 1), dict(B=0),
+                                  dict(causal=3), dict(scale=math.nan)])
+def test_ex_invalid(over):
+    assert call_ex(**over) == ta.TA_ERR_INVALID_ARG
+
+
+@host_only
+@pytest.mark.parametrize("d,dv", [(64, 32), (32, 64), (128, 256), (96, 128)])
+def test_ex_unsupported_widths(d, dv):
+    assert call_ex(d=d, dv=dv) == ta.TA_ERR_UNSUPPORTED
+
+
+@host_only
+@pytest.mark.parametrize("field,val", [("q", A + 8), ("v", A + 4), ("o", A + 8), ("lse", A + 2)])
+def test_ex_misaligned(field, val):
+    assert call_ex(**{field: val}) == ta.TA_ERR_MISALIGNED
+
+
+@host_only
+def test_ex_no_queries_is_a_no_op():
+    # every argument valid; Nq = 0 returns before any HIP call, NULL allowed for empty tensors
+    assert call_ex(Nq=0) == ta.TA_OK
+    assert call_ex(Nq=0, q=0, o=0, lse=0) == ta.TA_OK
+
+
+@host_only
+@pytest.mark.parametrize("field", ["k", "v"])
+def test_ex_null_keys_only_when_empty(field):
+    assert call_ex(**{field: 0}) == ta.TA_ERR_INVALID_ARG
+
+
+@host_only
+def test_square_entry_rejects_empty():
+    assert call(N=0) == ta.TA_ERR_INVALID_ARG

@@ -245,3 +245,60 @@ def test_recurrence_without_safe_max_gives_nan_on_hidden_rows():
         oo, _ = online_attention_ref(q, k, v, 1.0, [0, 1, 3], True, query_offset=-1)
     assert np.isnan(o[0]).any()
     assert not np.isnan(oo).any()
+
+
+# ---- general shapes: query offset, Nq != Nk, dv != d (sec. 22.7 lab conventions) ----
+
+GENERAL_CASES = [  # (nq, nk, d, dv, offset, causal)
+    (1, 9, 4, 3, 8, True),      # one decoding step at the last position
+    (3, 11, 5, 2, 4, True),     # a chunk of queries in the middle
+    (7, 4, 3, 6, 0, True),      # more queries than keys: later rows see every key
+    (6, 6, 4, 4, 2, True),
+    (5, 8, 2, 7, 0, False),
+]
+
+
+@pytest.mark.parametrize("case", GENERAL_CASES)
+def test_general_shapes_match_torch(case):
+    """Offset causal mask, Nq != Nk and dv != d against torch's float64 SDPA
+    with an explicit boolean mask (key j visible iff j <= i + offset)."""
+    import torch.nn.functional as F
+    nq, nk, d, dv, off, causal = case
+    rng = np.random.default_rng(60 + nq + nk)
+    q, k, v = (rng.standard_normal(s) for s in ((nq, d), (nk, d), (nk, dv)))
+    mask = torch.from_numpy(np.arange(nk)[None, :] <= np.arange(nq)[:, None] + off) if causal else None
+    ref = F.scaled_dot_product_attention(torch.from_numpy(q)[None], torch.from_numpy(k)[None],
+                                         torch.from_numpy(v)[None], attn_mask=mask, scale=0.45)[0]
+    o, lse = attention_ref(q, k, v, 0.45, causal, query_offset=off)
+    np.testing.assert_allclose(o, ref.numpy(), rtol=0, atol=1e-12)
+    s = 0.45 * q @ k.T
+    if causal:
+        s = np.where(mask.numpy(), s, -np.inf)
+    np.testing.assert_allclose(lse, np.log(np.exp(s).sum(axis=1)), rtol=0, atol=1e-12)
+
+
+def test_query_chunk_equals_rows_of_full_problem():
+    """Queries at positions off .. off+nq-1 against nk = off + nq keys give the
+    last nq rows of the square causal problem (decoding-style subproblem)."""
+    rng = np.random.default_rng(70)
+    n, nq = 13, 4
+    q, k, v = (rng.standard_normal((n, 3)) for _ in range(3))
+    full_o, full_l = attention_ref(q, k, v, 0.8, True)
+    o, lse = attention_ref(q[n - nq:], k, v, 0.8, True, query_offset=n - nq)
+    np.testing.assert_allclose(o, full_o[n - nq:], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, full_l[n - nq:], rtol=0, atol=1e-14)
+
+
+def test_offset_past_last_key_is_unmasked():
+    rng = np.random.default_rng(71)
+    q, k, v = rng.standard_normal((4, 3)), rng.standard_normal((6, 3)), rng.standard_normal((6, 2))
+    a = attention_ref(q, k, v, 0.7, True, query_offset=5)
+    b = attention_ref(q, k, v, 0.7, False)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(x, y, rtol=0, atol=1e-15)
+
+
+def test_no_keys_policy():
+    o, lse = attention_ref(np.ones((3, 4)), np.zeros((0, 4)), np.zeros((0, 2)), 0.5, True,
+                           query_offset=1)
+    assert o.shape == (3, 2) and np.all(o == 0) and np.all(np.isneginf(lse))

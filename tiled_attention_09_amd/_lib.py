@@ -34,6 +34,9 @@ def load_library() -> ctypes.CDLL:
         lib.attn_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
         lib.attn_fwd.restype = ctypes.c_int
+        lib.attn_fwd_ex.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 7 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+        lib.attn_fwd_ex.restype = ctypes.c_int
         lib.attn_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 4 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
         lib.attn_bwd.restype = ctypes.c_int
@@ -91,6 +94,53 @@ def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None
                       B, H, N, d, ctypes.c_float(float(scale)), int(bool(causal)), int(stream))
     if st != TA_OK:
         raise RuntimeError("attn_fwd failed: %s (status %d)" % (attn_status_string(st), st))
+    return out, lse
+
+
+def attn_fwd_ex_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, H: int,
+                    Nq: int, Nk: int, d: int, dv: int, query_offset: int, scale: float,
+                    causal: int, stream: int = 0) -> int:
+    """Call the general-shape C entry point with raw addresses; returns the status."""
+    return load_library().attn_fwd_ex(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Nq, Nk, d, dv,
+                                      query_offset, ctypes.c_float(scale), causal, stream)
+
+
+def attn_fwd_ex(q, k, v, scale: float | None = None, causal: bool = False, query_offset: int = 0,
+                out=None, lse=None, stream=None):
+    """Attention forward for general shapes on the GPU.
+
+    q: bf16 [B, H, Nq, d]; k: bf16 [B, H, Nk, d]; v: bf16 [B, H, Nk, dv] (device,
+    contiguous).  Queries sit at absolute positions query_offset + i (causal rule:
+    key j visible iff j <= i + query_offset).  Returns (o float32 [B, H, Nq, dv],
+    lse float32 [B, H, Nq]); rows that see no key get o = 0 and lse = -inf.
+    """
+    import torch
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or t.dtype != torch.bfloat16 or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous bfloat16 device tensor [B, H, rows, width]"
+                             % name)
+    B, H, Nq, d = (int(x) for x in q.shape)
+    if tuple(k.shape[:2]) != (B, H) or int(k.shape[3]) != d or tuple(v.shape[:3]) != tuple(k.shape[:3]):
+        raise ValueError("k must be [B, H, Nk, d] and v [B, H, Nk, dv]")
+    Nk, dv = int(k.shape[2]), int(v.shape[3])
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, Nq, dv), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if out.shape != (B, H, Nq, dv) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be contiguous float32 [B, H, Nq, dv]")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, Nq]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = lib.attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                         B, H, Nq, Nk, d, dv, int(query_offset), ctypes.c_float(float(scale)),
+                         int(bool(causal)), int(stream))
+    if st != TA_OK:
+        raise RuntimeError("attn_fwd_ex failed: %s (status %d)" % (attn_status_string(st), st))
     return out, lse
 
 

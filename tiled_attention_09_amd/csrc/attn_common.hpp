@@ -115,22 +115,34 @@ __device__ __forceinline__ void map_block(int bid, int bh_count, int n_t, bool r
 }
 
 // Enqueue the copy of row tile j of two matrices (K and V; Q and dO) into one
-// LDS stage.  Load i of wave w fills bytes [(W i + w) * 1024, +1024) (W waves) of the
-// stage's tile, one 16-byte chunk per lane; src_off holds each lane's offset
-// within a tile (tile_src_offsets).
+// LDS stage; the matrices may have different widths DA, DB (64 or 128).  Load
+// i of wave w fills bytes [(W i + w) * 1024, +1024) (W waves) of a stage's
+// tile, one 16-byte chunk per lane; src_a / src_b hold each lane's offset
+// within a tile (tile_src_offsets).  Copies of the two matrices alternate.
+template <int DA, int DB>
+__device__ __forceinline__ void issue_pair(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                           const uint32_t* src_a, const uint32_t* src_b, int j,
+                                           int wave, TA_LDS uint16_t* da, TA_LDS uint16_t* db) {
+  constexpr int LA = Tile<DA>::LOADS, LB = Tile<DB>::LOADS;
+  const uint32_t off_a = (uint32_t)j * (uint32_t)Tile<DA>::BYTES;   // scalar
+  const uint32_t off_b = (uint32_t)j * (uint32_t)Tile<DB>::BYTES;
+#pragma unroll
+  for (int i = 0; i < (LA > LB ? LA : LB); ++i) {
+    const int dst = (kWaves * i + wave) * 512;   // uint16 elements, wave-uniform
+    if (i < LA)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (TA_LDS void*)(da + dst), 16, src_a[i], off_a,
+                                               0, 0);
+    if (i < LB)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (TA_LDS void*)(db + dst), 16, src_b[i], off_b,
+                                               0, 0);
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
                                            const uint32_t* src_off, int j, int wave,
                                            TA_LDS uint16_t* kd, TA_LDS uint16_t* vd) {
-  const uint32_t tile_off = (uint32_t)j * (uint32_t)Tile<D>::BYTES;   // scalar
-#pragma unroll
-  for (int i = 0; i < Tile<D>::LOADS; ++i) {
-    const int dst = (kWaves * i + wave) * 512;   // uint16 elements, wave-uniform
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (TA_LDS void*)(kd + dst), 16, src_off[i],
-                                             tile_off, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (TA_LDS void*)(vd + dst), 16, src_off[i],
-                                             tile_off, 0, 0);
-  }
+  issue_pair<D, D>(kr, vr, src_off, src_off, j, wave, kd, vd);
 }
 
 // Per-lane source offsets of issue_tile: LDS chunk p = (W i + w) * 64 + lane

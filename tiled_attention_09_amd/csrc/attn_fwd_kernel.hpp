@@ -36,25 +36,38 @@
 //    group receives a 16(d) x 4(keys) block transposed, which is exactly the
 //    V^T operand, and the 4 key rows of a half-wave land in 4 different 64-byte
 //    bank groups.
-//  * Causal: a query tile visits key tiles only up to its last row; a wave
-//    whose rows all precede a key tile skips its math; element masks are
-//    applied only on tiles that cross the diagonal or the end of the sequence.
+//  * Causal: a query tile visits key tiles only up to its last row's position
+//    (query index plus the offset of the lab's decoding-style subproblems); a
+//    wave whose rows all precede a key tile skips its math; element masks are
+//    applied only on tiles that cross the diagonal or the end of the keys.
+//  * General shapes: Nq queries and Nk keys per head, Q/K rows of width D and
+//    V/O rows of width DV; with no keys a row keeps l = 0 and gets O = 0,
+//    LSE = -inf (the lab's fully-hidden-row policy).
 #pragma once
 
 #include "attn_common.hpp"
 
 namespace tiledattn {
 
-template <int D, bool CAUSAL, bool POS_SCALE>
+// D: width of Q and K rows; DV: width of V and O rows.  Nq query rows at
+// absolute positions offset .. offset + Nq - 1 attend Nk keys at positions
+// 0 .. Nk - 1 (causal: key j visible to query i iff j <= i + offset).
+// GENERAL = false is the square case (Nk = Nq, offset 0) with those facts
+// known at compile time.
+template <int D, int DV, bool CAUSAL, bool POS_SCALE, bool GENERAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, float* __restrict__ O,
-                     float* __restrict__ LSE, int bh_count, int N, int n_qt, float scale_log2) {
+                     float* __restrict__ LSE, int bh_count, int Nq, int nk_arg, int offset_arg,
+                     int n_qt, float scale_log2) {
+  const int Nk = GENERAL ? nk_arg : Nq;
+  const int offset = GENERAL ? offset_arg : 0;
   using T = Tile<D>;
+  using TV = Tile<DV>;
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[kBN * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[kBN * DV];
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[kBN * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[kBN * DV];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -65,11 +78,9 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   int bh, qt;
   map_block(blockIdx.x, bh_count, n_qt, CAUSAL, bh, qt);
 
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2u;
-  const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + (size_t)bh * Nq * D, (uint32_t)Nq * D * 2u);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + (size_t)bh * Nk * D, (uint32_t)Nk * D * 2u);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + (size_t)bh * Nk * DV, (uint32_t)Nk * DV * 2u);
 
   const int q0 = qt * kBM + wave * 32;   // first query row of this wave
   const int my_q = q0 + l32;             // this lane's query row
@@ -80,16 +91,18 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   for (int ks = 0; ks < T::KS; ++ks)
     qf[ks] = __builtin_bit_cast(bf16x8, load16(qr, (uint32_t)(my_q * D + 16 * ks + 8 * hi) * 2u));
 
-  // Tile copy offsets: the same for every tile and for K and V.
-  uint32_t src_off[T::LOADS];
-  tile_src_offsets<D>(src_off, wave, lane);
+  // Tile copy offsets: the same for every tile (K and V differ only when D != DV).
+  uint32_t src_k[T::LOADS], src_v[TV::LOADS];
+  tile_src_offsets<D>(src_k, wave, lane);
+  tile_src_offsets<DV>(src_v, wave, lane);
   // Operand reads: K row-wise (A operand of S^T), V transposed (A operand of
   // O^T), with lane offsets whose row/stage parts fold into the instruction.
   const LdsReader<D> rd(lane);
+  const LdsReader<DV> rdv(lane);
 
-  f32x16 oacc[T::DB];
+  f32x16 oacc[TV::DB];
 #pragma unroll
-  for (int db = 0; db < T::DB; ++db)
+  for (int db = 0; db < TV::DB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   // Running max: raw-score domain when the scale is positive (max commutes
@@ -97,8 +110,10 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   float m = -__builtin_inff();
   float l = 0.f;               // running normaliser (this wave half's keys)
 
-  const int n_kt_all = (N + kBN - 1) / kBN;
-  const int n_kt = CAUSAL ? min(n_kt_all, (qt + 1) * (kBM / kBN)) : n_kt_all;
+  // Key tiles this query tile can see (causal: up to its last row's position).
+  const int n_kt_all = (Nk + kBN - 1) / kBN;
+  const int n_kt = CAUSAL ? min(n_kt_all, (qt * kBM + kBM + offset + kBN - 1) / kBN) : n_kt_all;
+  const int q_last = q0 + 31 + offset;   // position of the wave's last query row
 
   auto compute_tile = [&](int j, const TA_LDS uint16_t* kt, const TA_LDS uint16_t* vt) {
     const int key0 = j * kBN;
@@ -125,7 +140,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     __builtin_amdgcn_s_setprio(0);
 
     // Hide future / non-existent keys (only tiles crossing the diagonal or the end).
-    const bool edge = (CAUSAL && key0 + kBN - 1 > q0) || (key0 + kBN > N);
+    const bool edge = (CAUSAL && key0 + kBN - 1 > q0 + offset) || (key0 + kBN > Nk);
     if (!POS_SCALE) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -138,7 +153,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = key0 + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-          if ((CAUSAL && key > my_q) || key >= N) s[kb][i] = -__builtin_inff();
+          if ((CAUSAL && key > my_q + offset) || key >= Nk) s[kb][i] = -__builtin_inff();
         }
     }
 
@@ -161,7 +176,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
       l *= alpha;
 #pragma unroll
-      for (int db = 0; db < T::DB; ++db)
+      for (int db = 0; db < TV::DB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
     }
@@ -186,8 +201,8 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int db = 0; db < T::DB; ++db) {
-        const bf16x8 a = rd.col_op(vt, g, db);
+      for (int db = 0; db < TV::DB; ++db) {
+        const bf16x8 a = rdv.col_op(vt, g, db);
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[g], oacc[db], 0, 0, 0);
       }
   };
@@ -197,26 +212,29 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   TA_LDS uint16_t* const v0 = (TA_LDS uint16_t*)v_lds0;
   TA_LDS uint16_t* const k1 = (TA_LDS uint16_t*)k_lds1;
   TA_LDS uint16_t* const v1 = (TA_LDS uint16_t*)v_lds1;
-  issue_tile<D>(kr, vr, src_off, 0, wave, k0, v0);
+  if (n_kt > 0) issue_pair<D, DV>(kr, vr, src_k, src_v, 0, wave, k0, v0);
   for (int j = 0; j < n_kt; j += 2) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();                       // tile j visible; tile j-1's readers done
-    if (j + 1 < n_kt) issue_tile<D>(kr, vr, src_off, j + 1, wave, k1, v1);
-    if (!(CAUSAL && j * kBN > q0 + 31)) compute_tile(j, k0, v0);
+    if (j + 1 < n_kt) issue_pair<D, DV>(kr, vr, src_k, src_v, j + 1, wave, k1, v1);
+    if (!(CAUSAL && j * kBN > q_last)) compute_tile(j, k0, v0);
     if (j + 1 >= n_kt) break;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (j + 2 < n_kt) issue_tile<D>(kr, vr, src_off, j + 2, wave, k0, v0);
-    if (!(CAUSAL && (j + 1) * kBN > q0 + 31)) compute_tile(j + 1, k1, v1);
+    if (j + 2 < n_kt) issue_pair<D, DV>(kr, vr, src_k, src_v, j + 2, wave, k0, v0);
+    if (!(CAUSAL && (j + 1) * kBN > q_last)) compute_tile(j + 1, k1, v1);
   }
 
-  // Epilogue: combine the two halves' normalisers, O = o / l, LSE = m + log2 l (as ln).
+  // Epilogue: combine the two halves' normalisers, O = o / l, LSE = m + log2 l
+  // (as ln).  A row that saw no key (no keys at all) follows the lab's policy:
+  // O = 0 and LSE = -inf.
   const float l_row = l + other_half(l);
-  if (my_q < N) {
-    const float inv = 1.f / l_row;
-    float* orow = O + head + (size_t)my_q * D;
+  if (my_q < Nq) {
+    const bool live = l_row > 0.f;
+    const float inv = live ? 1.f / l_row : 0.f;
+    float* orow = O + ((size_t)bh * Nq + my_q) * DV;
 #pragma unroll
-    for (int db = 0; db < T::DB; ++db)
+    for (int db = 0; db < TV::DB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         f32x4 val = {oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv,
@@ -224,7 +242,8 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * g + 4 * hi) = val;
       }
     const float mlog2 = POS_SCALE ? m * scale_log2 : m;
-    if (hi == 0) LSE[(size_t)bh * N + my_q] = (mlog2 + __log2f(l_row)) * kLn2;
+    if (hi == 0)
+      LSE[(size_t)bh * Nq + my_q] = live ? (mlog2 + __log2f(l_row)) * kLn2 : -__builtin_inff();
   }
 }
 
