@@ -99,6 +99,27 @@ __device__ __forceinline__ void sched_mfma_ds(std::integer_sequence<int, I...>) 
    ...);
 }
 
+// Recipe building blocks: a group of R DS reads, and N repetitions of
+// (1 MFMA, R DS reads, V VALU instructions); empty groups are skipped.
+template <int R>
+__device__ __forceinline__ void sched_reads() {
+  if (R) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+}
+template <int R, int V>
+__device__ __forceinline__ void sched_step() {
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  if (R) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+  if (V) __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+}
+template <int R, int V, int... I>
+__device__ __forceinline__ void sched_rep_impl(std::integer_sequence<int, I...>) {
+  ((sched_step<R, V>(), (void)I), ...);
+}
+template <int R, int V, int N>
+__device__ __forceinline__ void sched_rep() {
+  sched_rep_impl<R, V>(std::make_integer_sequence<int, N>{});
+}
+
 // Workgroup -> (head, row tile).  Workgroups are handed to the 8 XCDs
 // round-robin, so block b runs on XCD b % 8; consecutive logical indices are
 // given to the same XCD so one head's tiles share that XCD's L2.  With
@@ -136,6 +157,17 @@ __device__ __forceinline__ void issue_pair(__amdgpu_buffer_rsrc_t ra, __amdgpu_b
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (TA_LDS void*)(db + dst), 16, src_b[i], off_b,
                                                0, 0);
   }
+}
+
+// One matrix's row tile j into an LDS stage (same placement as issue_pair).
+template <int D>
+__device__ __forceinline__ void issue_rows(__amdgpu_buffer_rsrc_t r, const uint32_t* src, int j,
+                                           int wave, TA_LDS uint16_t* dst_tile) {
+  const uint32_t off = (uint32_t)j * (uint32_t)Tile<D>::BYTES;   // scalar
+#pragma unroll
+  for (int i = 0; i < Tile<D>::LOADS; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (TA_LDS void*)(dst_tile + (kWaves * i + wave) * 512),
+                                             16, src[i], off, 0, 0);
 }
 
 template <int D>

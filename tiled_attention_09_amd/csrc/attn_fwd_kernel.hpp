@@ -49,6 +49,10 @@
 
 namespace tiledattn {
 
+#ifndef TA_FWD_VALU_PER_MFMA
+#define TA_FWD_VALU_PER_MFMA 7
+#endif
+
 // D: width of Q and K rows; DV: width of V and O rows.  Nq query rows at
 // absolute positions offset .. offset + Nq - 1 attend Nk keys at positions
 // 0 .. Nk - 1 (causal: key j visible to query i iff j <= i + offset).
@@ -115,14 +119,13 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const int n_kt = CAUSAL ? min(n_kt_all, (qt * kBM + kBM + offset + kBN - 1) / kBN) : n_kt_all;
   const int q_last = q0 + 31 + offset;   // position of the wave's last query row
 
-  auto compute_tile = [&](int j, const TA_LDS uint16_t* kt, const TA_LDS uint16_t* vt) {
-    const int key0 = j * kBN;
-    // S^T (64 keys x 32 queries): block kb covers keys key0 + 32 kb + [0, 32).
-    // The wave's matrix work runs at raised priority, so that when the other
-    // workgroup's wave on this SIMD is in its softmax, the MFMAs are not held
-    // back behind its vector instructions.
-    f32x16 s[2];
-    __builtin_amdgcn_s_setprio(1);
+  // Tiles this wave takes part in: key tiles whose first key is not past the
+  // wave's last query position (a prefix of 0 .. n_kt - 1).
+  const int n_w = CAUSAL ? min(n_kt, q_last / kBN + 1) : n_kt;
+
+  // S^T (64 keys x 32 queries) of the key tile in `kt`: block kb covers tile
+  // keys 32 kb + [0, 32).
+  auto scores = [&](const TA_LDS uint16_t* kt, f32x16 (&s)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -130,24 +133,23 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #pragma unroll
     for (int ks = 0; ks < T::KS; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = rd.row_op(kt, kb, ks);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
-      }
-    // Issue order: the K operands of four MFMAs ahead, then one MFMA per read,
-    // so each read has ~4 MFMA times (~128 cycles) to return from LDS.
-    sched_qk<T::KS>(std::make_integer_sequence<int, 2 * T::KS>{});
-    __builtin_amdgcn_s_setprio(0);
+      for (int kb = 0; kb < 2; ++kb)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.row_op(kt, kb, ks), qf[ks], s[kb], 0, 0,
+                                                        0);
+  };
 
-    // Hide future / non-existent keys (only tiles crossing the diagonal or the end).
-    const bool edge = (CAUSAL && key0 + kBN - 1 > q0 + offset) || (key0 + kBN > Nk);
+  // Scale (non-positive scales only) and hide future / non-existent keys of key
+  // tile j in s; only tiles crossing the diagonal or the end of the keys need
+  // the mask.
+  auto prepare = [&](int j, f32x16 (&s)[2]) __attribute__((always_inline)) {
+    const int key0 = j * kBN;
     if (!POS_SCALE) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[kb][i] *= scale_log2;
     }
-    if (edge) {
+    if ((CAUSAL && key0 + kBN - 1 > q0 + offset) || (key0 + kBN > Nk)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -156,7 +158,12 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
           if ((CAUSAL && key > my_q + offset) || key >= Nk) s[kb][i] = -__builtin_inff();
         }
     }
+  };
 
+  // Online-softmax update from a tile's prepared scores s:
+  // m' = max(m, max S), alpha = exp(m - m'), p = exp(S - m'), l' = alpha l + sum p.
+  // Returns alpha; p goes to pf as the bf16 B operand of the value product.
+  auto softmax = [&](f32x16 (&s)[2], bf16x8 (&pf)[4]) __attribute__((always_inline)) {
     // Row maximum: 32 in-lane values (a chain of 3-input maxima), then the
     // other wave half.
     float mx = fmaxf(s[0][0], s[0][1]);
@@ -164,28 +171,16 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     for (int i = 2; i < 32; i += 2)
       mx = fmaxf(fmaxf(mx, s[i >> 4][i & 15]), s[(i + 1) >> 4][(i + 1) & 15]);
     mx = fmaxf(mx, other_half(mx));
-
-    // m' = max(m, max S) and alpha = exp(m - m') (in log2 units); the safe
-    // reference keeps a row with no visible key yet away from -inf - -inf.
+    // The safe reference keeps a row with no visible key yet away from -inf - -inf.
     const float m_new = fmaxf(m, mx);
     const float ref = (m_new == -__builtin_inff()) ? 0.f : m_new;
     const float cref = POS_SCALE ? ref * scale_log2 : ref;
     const float alpha = __builtin_amdgcn_exp2f((POS_SCALE ? m * scale_log2 : m) - cref);
     m = m_new;
-    // Rescale l and o only when some row of this wave moved its maximum.
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < TV::DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-    }
-
     // p = 2^(c s - c m'); positive scale: one fused multiply-add per element.
     // The row maximum itself gets p = 1 exactly, so the dominant weight carries
     // no bf16 rounding into the value product.
     float psum = 0.f;
-    bf16x8 pf[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -195,34 +190,88 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         psum += p;
         pf[kb * 2 + (i >> 3)][i & 7] = (__bf16)p;
       }
-    l += psum;
+    l = __builtin_fmaf(l, alpha, psum);
+    return alpha;
+  };
 
-    // O^T (d x 32 queries) += V^T (d x 64 keys) P^T (64 keys x 32 queries).
+  // O^T (dv x 32 queries) += V^T (dv x 64 keys) P^T (64 keys x 32 queries).
+  auto values = [&](const TA_LDS uint16_t* vt, const bf16x8 (&pf)[4])
+                    __attribute__((always_inline)) {
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int db = 0; db < TV::DB; ++db) {
-        const bf16x8 a = rdv.col_op(vt, g, db);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[g], oacc[db], 0, 0, 0);
-      }
+      for (int db = 0; db < TV::DB; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rdv.col_op(vt, g, db), pf[g], oacc[db],
+                                                           0, 0, 0);
+    sched_mfma_ds<8, 2, 8 * TV::DB>(std::make_integer_sequence<int, 4 * TV::DB>{});
   };
 
-  // Two-stage pipeline, unrolled by two so each stage's buffers are static.
+  // Pipeline (the matrix work of the next tile runs under the softmax of this
+  // one, inside the wave): K runs one tile ahead of V.  At iteration j, LDS
+  // holds K_{j+1} (for S_{j+1}) and V_j (for P_j V_j); the barrier at its start
+  // also frees K_j's and V_{j-1}'s stages, which receive K_{j+2} and V_{j+1}.
+  // Each iteration: S_{j+1} = K_{j+1} Q^T interleaved with the softmax of S_j,
+  // the alpha rescale of o (only when some row moved its maximum), then P_j V_j.
   TA_LDS uint16_t* const k0 = (TA_LDS uint16_t*)k_lds0;
   TA_LDS uint16_t* const v0 = (TA_LDS uint16_t*)v_lds0;
   TA_LDS uint16_t* const k1 = (TA_LDS uint16_t*)k_lds1;
   TA_LDS uint16_t* const v1 = (TA_LDS uint16_t*)v_lds1;
-  if (n_kt > 0) issue_pair<D, DV>(kr, vr, src_k, src_v, 0, wave, k0, v0);
-  for (int j = 0; j < n_kt; j += 2) {
+  f32x16 sa[2], sb[2];
+  bf16x8 pf[4];
+
+  auto step = [&](int j, const TA_LDS uint16_t* k_next, const TA_LDS uint16_t* v_cur,
+                  f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) __attribute__((always_inline)) {
+    prepare(j, s_cur);
+    // S_{j+1} is computed even when this wave has no tile j+1 (its last tile):
+    // the stage holds in-bounds data and the result is not used.
+    __builtin_amdgcn_s_setprio(1);
+    scores(k_next, s_next);
+    const float alpha = softmax(s_cur, pf);
+    // Issue order: four K operand reads ahead, then each product followed by
+    // one read and a share of the softmax's vector instructions.
+    sched_reads<4>();
+    sched_rep<1, TA_FWD_VALU_PER_MFMA, 2 * T::KS - 4>();
+    sched_rep<0, TA_FWD_VALU_PER_MFMA, 4>();
+    // The probabilities must be complete here, inside the region shared with
+    // the score products: without this use the compiler sinks the
+    // exponentials below the rescale branch, out of reach of the interleave.
+    asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(pf[2]), "v"(pf[3]));
+    __builtin_amdgcn_s_setprio(0);
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < TV::DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    }
+    values(v_cur, pf);
+  };
+  // Iteration j with the stage parity P = j % 2 fixed at compile time.
+  auto iter = [&](int j, auto pc) __attribute__((always_inline)) {
+    constexpr int P = decltype(pc)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();                       // tile j visible; tile j-1's readers done
-    if (j + 1 < n_kt) issue_pair<D, DV>(kr, vr, src_k, src_v, j + 1, wave, k1, v1);
-    if (!(CAUSAL && j * kBN > q_last)) compute_tile(j, k0, v0);
-    if (j + 1 >= n_kt) break;
+    __syncthreads();                 // K_{j+1}, V_j visible; K_j, V_{j-1} stages free
+    if (j + 2 < n_kt) issue_rows<D>(kr, src_k, j + 2, wave, P ? k1 : k0);
+    if (j + 1 < n_kt) issue_rows<DV>(vr, src_v, j + 1, wave, P ? v0 : v1);
+    if (j < n_w) {
+      if constexpr (P == 0)
+        step(j, k1, v0, sa, sb);
+      else
+        step(j, k0, v1, sb, sa);
+    }
+  };
+
+  if (n_kt > 0) {
+    issue_rows<D>(kr, src_k, 0, wave, k0);
+    issue_rows<DV>(vr, src_v, 0, wave, v0);
+    if (n_kt > 1) issue_rows<D>(kr, src_k, 1, wave, k1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (j + 2 < n_kt) issue_pair<D, DV>(kr, vr, src_k, src_v, j + 2, wave, k0, v0);
-    if (!(CAUSAL && (j + 1) * kBN > q_last)) compute_tile(j + 1, k1, v1);
+    if (n_w > 0) scores(k0, sa);
+  }
+  for (int j = 0; j < n_kt; j += 2) {
+    iter(j, std::integral_constant<int, 0>{});
+    if (j + 1 >= n_kt) break;
+    iter(j + 1, std::integral_constant<int, 1>{});
   }
 
   // Epilogue: combine the two halves' normalisers, O = o / l, LSE = m + log2 l
