@@ -72,18 +72,6 @@ __device__ __forceinline__ float other_half(float x) {
   return __int_as_float((threadIdx.x & 32) ? pr[0] : pr[1]);
 }
 
-// Issue-order recipe for the Q K^T block (group sizes must be compile-time
-// constants, hence the expansion over an index sequence): four operand reads
-// first, then alternately one MFMA and one read, the last four MFMAs at the end.
-constexpr int kSgMfma = 0x008;
-constexpr int kSgDsRead = 0x100;
-template <int KS, int... I>
-__device__ __forceinline__ void sched_qk(std::integer_sequence<int, I...>) {
-  __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4, 0);
-  ((__builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0),
-    __builtin_amdgcn_sched_group_barrier(kSgDsRead, I < 2 * KS - 4 ? 1 : 0, 0)), ...);
-}
-
 // Issue-order recipe for a block of NMFMA matrix products fed by LDS reads:
 // PRE reads first, then each product followed by up to PER more reads until
 // TOTAL reads are placed (group sizes must be compile-time constants, hence the

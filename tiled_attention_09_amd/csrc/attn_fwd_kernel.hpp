@@ -25,8 +25,11 @@
 //    the lane's own query, so the alpha rescale is lane-local.
 //  * K and V tiles are copied HBM/L2 -> LDS by the buffer unit itself
 //    (buffer_load ... lds, 16 bytes per lane, no VGPR staging), two stages
-//    deep: tile j+1 is in flight while tile j is multiplied; one barrier per
-//    tile.  The buffer range check returns zeros past the end of the head, so
+//    each, K one tile ahead of V; one barrier per tile.
+//  * Software pipeline inside the wave: while the softmax of tile j runs on
+//    the vector unit, the score products of tile j+1 run on the matrix unit
+//    (an explicit issue recipe interleaves them), then o is rescaled and
+//    P_j V_j accumulated.  The buffer range check returns zeros past the end of the head, so
 //    a ragged last tile needs no guard (zero V rows also keep 0 * garbage out
 //    of the sum).
 //  * Both tiles keep the row-major [key][d] layout with the 16-byte chunks of
@@ -49,9 +52,8 @@
 
 namespace tiledattn {
 
-#ifndef TA_FWD_VALU_PER_MFMA
-#define TA_FWD_VALU_PER_MFMA 7
-#endif
+// Vector instructions of the softmax placed after each score product.
+constexpr int kValuPerMfma = 7;
 
 // D: width of Q and K rows; DV: width of V and O rows.  Nq query rows at
 // absolute positions offset .. offset + Nq - 1 attend Nk keys at positions
@@ -203,6 +205,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       for (int db = 0; db < TV::DB; ++db)
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rdv.col_op(vt, g, db), pf[g], oacc[db],
                                                            0, 0, 0);
+    // Eight transposed V reads in flight, then two more per product.
     sched_mfma_ds<8, 2, 8 * TV::DB>(std::make_integer_sequence<int, 4 * TV::DB>{});
   };
 
@@ -224,14 +227,16 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     prepare(j, s_cur);
     // S_{j+1} is computed even when this wave has no tile j+1 (its last tile):
     // the stage holds in-bounds data and the result is not used.
+    // The shared region runs at raised wave priority, so the other wave on
+    // this SIMD (in its own value products) does not hold back its issue.
     __builtin_amdgcn_s_setprio(1);
     scores(k_next, s_next);
     const float alpha = softmax(s_cur, pf);
     // Issue order: four K operand reads ahead, then each product followed by
     // one read and a share of the softmax's vector instructions.
     sched_reads<4>();
-    sched_rep<1, TA_FWD_VALU_PER_MFMA, 2 * T::KS - 4>();
-    sched_rep<0, TA_FWD_VALU_PER_MFMA, 4>();
+    sched_rep<1, kValuPerMfma, 2 * T::KS - 4>();
+    sched_rep<0, kValuPerMfma, 4>();
     // The probabilities must be complete here, inside the region shared with
     // the score products: without this use the compiler sinks the
     // exponentials below the rescale branch, out of reach of the interleave.
