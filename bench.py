@@ -171,6 +171,63 @@ def time_backward(w, q, k, v, o, lse, stream, steps: int, warmup: int):
             "steps": steps, "warmup": warmup, "grad_dtype": "fp32", "dout_dtype": "bf16"}
 
 
+PEAK_FP8_TFLOPS = 5000.0        # MI355X dense fp8 MFMA, published
+
+
+def time_fp8(w, q, k, v, stream, steps: int, warmup: int):
+    """Time the FP8-score forward (attn_fwd_fp8) on the workload with Q and K
+    quantised beforehand (attn_quantize_fp8, timed separately).  Half of the
+    algorithmic flops (the scores) run at the fp8 rate and half (P V) at the
+    bf16 rate, so the roofline peak is the time-weighted combination
+    2 / (1/5000 + 1/2500) = 3333 TFLOP/s."""
+    import torch
+
+    import tiled_attention_09_amd as ta
+    dev = q.device
+    if w.d != 128:
+        return None
+    q8 = torch.empty(q.shape, dtype=torch.uint8, device=dev)
+    k8 = torch.empty(k.shape, dtype=torch.uint8, device=dev)
+    qd = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
+    kd = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
+    o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    sc = stream.cuda_stream
+
+    def quant():
+        ta.attn_quantize_fp8(q, out=q8, descale=qd, stream=sc)
+        ta.attn_quantize_fp8(k, out=k8, descale=kd, stream=sc)
+
+    def fwd():
+        ta.attn_fwd_fp8(q8, k8, v, qd, kd, w.scale, w.causal, out=o, lse=lse, stream=sc)
+
+    def timed(fn, n):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    quant_ms = timed(quant, steps)
+    ms = timed(fwd, steps)
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    peak = 2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_BF16_TFLOPS)
+    qbytes = 2 * (w.B * w.H * w.N * w.d * 3 + w.B * w.H * 8)   # Q and K: read bf16, write codes
+    return {"metric": "attention fwd TFLOP/s with FP8 scores (Q, K as E4M3 codes, per-head descale)",
+            "value": round(tflops, 2), "unit": "TFLOP/s", "kernel_ms": round(ms, 5),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": round(peak, 1),
+                         "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None},
+            "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "quantize_q_and_k_ms": round(quant_ms, 5),
+            "quantize_gbs": round(qbytes / (quant_ms * 1e-3) / 1e9, 1),
+            "steps": steps, "warmup": warmup}
+
+
 # General-shape forward workloads (attn_fwd_ex): name, B, H, Nq, Nk, d, dv, offset, causal.
 GENERAL = [
     ("chunked prefill: 1024 queries at positions 7168.. of 8192 keys", 2, 32, 1024, 8192, 128, 128,
@@ -240,6 +297,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-general", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--counter-pass", action="store_true",
                     help="run the calibration copy and a few launches for rocprofv3 --pmc")
     args = ap.parse_args()
@@ -334,6 +392,8 @@ def main():
     }
     if not args.no_backward:
         out["backward"] = time_backward(w, q, k, v, o, lse, stream, args.steps, args.warmup)
+    if not args.no_fp8:
+        out["fp8_scores"] = time_fp8(w, q, k, v, stream, args.steps, args.warmup)
     if not args.no_general:
         del q, k, v, o, lse
         torch.cuda.empty_cache()

@@ -99,6 +99,49 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, float* o, float* ls
                 float scale, int causal, void* stream);
 
 /*
+ * attn_quantize_fp8 -- per-head FP8 quantisation of bf16 rows (the input side of
+ * attn_fwd_fp8).  For each head h of x (heads x rows x d, contiguous):
+ *
+ *     amax      = max |x[h]|
+ *     out[h]    = RNE_e4m3(clamp(x[h] * (448 / amax), -448, 448))   OCP E4M3 codes
+ *     descale[h] = amax / 448        (1 when amax = 0)
+ *
+ * each step one float32 operation, so x ~= e4m3(out) * descale.  (Page
+ * "Chapter 7 GPU Kernels: CUDA, HIP & Triton", sec. 7.6.2: FP8 Q K^T with
+ * online descaling; the per-head amax recipe is this library's choice.)
+ *
+ *   x       : device bf16 [heads, rows, d], read only, 16-byte aligned.
+ *   out     : device uint8 [heads, rows, d], written, 16-byte aligned.
+ *   descale : device float32 [heads], written (used as scratch while running).
+ *   heads   : 1 .. 65535;  rows: 1 .. 2^22;  d: 64 or 128 (TA_ERR_UNSUPPORTED).
+ *   stream  : as for attn_fwd.  Finite inputs are a precondition.
+ * Errors, ownership and synchronisation as for attn_fwd.
+ */
+int attn_quantize_fp8(const void* x, void* out, float* descale, int heads, int rows, int d,
+                      void* stream);
+
+/*
+ * attn_fwd_fp8 -- attn_fwd with FP8 scores: Q and K arrive as OCP E4M3 codes
+ * with per-(batch, head) descale factors, so the scores are
+ *
+ *     S[i,j] = scale * q_descale[b,h] * k_descale[b,h] * <q8_i, k8_j>
+ *
+ * computed on the FP8 matrix unit (32x32x64 products at twice the bf16 rate)
+ * with the descales folded into the softmax's exponent scale; P V stays in
+ * bf16 with fp32 accumulation; O and LSE as for attn_fwd.
+ *
+ *   q8, k8    : device uint8 [B, H, N, d] E4M3 codes (attn_quantize_fp8 output).
+ *   v         : device bf16 [B, H, N, d].
+ *   q_descale, k_descale : device float32 [B, H].
+ *   d         : 128 only (TA_ERR_UNSUPPORTED otherwise).
+ *   o, lse, B, H, N, scale, causal, stream, errors: as for attn_fwd
+ *   (q8, k8, v, o 16-byte aligned; lse and the descales 4-byte aligned).
+ */
+int attn_fwd_fp8(const void* q8, const void* k8, const void* v, float* o, float* lse,
+                 const float* q_descale, const float* k_descale, int B, int H, int N, int d,
+                 float scale, int causal, void* stream);
+
+/*
  * attn_bwd_workspace_size -- bytes of device workspace attn_bwd needs for
  * (B, H, N): 8 * B * H * (N rounded up to even).  Returns 0 when the sizes are
  * out of the range attn_bwd accepts.

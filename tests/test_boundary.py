@@ -41,7 +41,8 @@ def declared_functions():
 
 def test_header_declares_entry_points():
     assert declared_functions() == ["attn_bwd", "attn_bwd_workspace_size", "attn_fwd",
-                                    "attn_fwd_ex", "attn_status_string"]
+                                    "attn_fwd_ex", "attn_fwd_fp8", "attn_quantize_fp8",
+                                    "attn_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -219,3 +220,51 @@ def test_ex_null_keys_only_when_empty(field):
 @host_only
 def test_square_entry_rejects_empty():
     assert call(N=0) == ta.TA_ERR_INVALID_ARG
+
+
+# ---- FP8 entry points -----------------------------------------------------------
+
+FP8_PTRS = ["q", "k", "v", "o", "lse", "qd", "kd"]
+
+
+def call_fp8(**over):
+    args = dict({p: A for p in FP8_PTRS}, B=1, H=2, N=256, d=128, scale=0.09, causal=1)
+    args.update(over)
+    return ta.attn_fwd_fp8_raw(*(args[p] for p in FP8_PTRS), args["B"], args["H"], args["N"],
+                               args["d"], args["scale"], args["causal"], 0)
+
+
+@host_only
+@pytest.mark.parametrize("field", FP8_PTRS)
+def test_fp8_null_pointer(field):
+    assert call_fp8(**{field: 0}) == ta.TA_ERR_INVALID_ARG
+
+
+@host_only
+@pytest.mark.parametrize("over", [dict(N=0), dict(B=0), dict(causal=5), dict(scale=math.inf)])
+def test_fp8_invalid(over):
+    assert call_fp8(**over) == ta.TA_ERR_INVALID_ARG
+
+
+@host_only
+def test_fp8_only_d128():
+    assert call_fp8(d=64) == ta.TA_ERR_UNSUPPORTED
+
+
+@host_only
+@pytest.mark.parametrize("field,off", [("q", 8), ("k", 4), ("v", 8), ("o", 8), ("lse", 2),
+                                       ("qd", 2), ("kd", 1)])
+def test_fp8_misaligned(field, off):
+    assert call_fp8(**{field: A + off}) == ta.TA_ERR_MISALIGNED
+
+
+@host_only
+def test_quantize_validation():
+    lib = ta.load_library()
+    q = lambda x=A, o=A, dsc=A, heads=2, rows=16, d=64: lib.attn_quantize_fp8(x, o, dsc, heads, rows, d, 0)
+    assert q(x=0) == ta.TA_ERR_INVALID_ARG
+    assert q(heads=0) == ta.TA_ERR_INVALID_ARG
+    assert q(rows=0) == ta.TA_ERR_INVALID_ARG
+    assert q(d=96) == ta.TA_ERR_UNSUPPORTED
+    assert q(o=A + 8) == ta.TA_ERR_MISALIGNED
+    assert q(dsc=A + 2) == ta.TA_ERR_MISALIGNED

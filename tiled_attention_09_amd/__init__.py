@@ -8,9 +8,11 @@ the HIP kernels of ``csrc/`` through the C ABI of ``include/tiledattn.h``
 """
 from ._lib import (TA_ERR_HIP, TA_ERR_INVALID_ARG, TA_ERR_MISALIGNED, TA_ERR_UNSUPPORTED, TA_OK,
                    attn_bwd, attn_bwd_raw, attn_bwd_workspace_size, attn_fwd, attn_fwd_ex,
-                   attn_fwd_ex_raw, attn_fwd_raw,
+                   attn_fwd_ex_raw, attn_fwd_fp8, attn_fwd_fp8_raw, attn_fwd_raw,
+                   attn_quantize_fp8,
                    attn_status_string, library_path, load_library)
 
-__all__ = ["attn_fwd", "attn_fwd_raw", "attn_fwd_ex", "attn_fwd_ex_raw", "attn_bwd", "attn_bwd_raw", "attn_bwd_workspace_size",
+__all__ = ["attn_fwd", "attn_fwd_raw", "attn_fwd_ex", "attn_fwd_ex_raw", "attn_fwd_fp8",
+           "attn_fwd_fp8_raw", "attn_quantize_fp8", "attn_bwd", "attn_bwd_raw", "attn_bwd_workspace_size",
            "attn_status_string", "library_path", "load_library",
            "TA_OK", "TA_ERR_INVALID_ARG", "TA_ERR_UNSUPPORTED", "TA_ERR_MISALIGNED", "TA_ERR_HIP"]

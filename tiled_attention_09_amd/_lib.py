@@ -42,6 +42,12 @@ def load_library() -> ctypes.CDLL:
         lib.attn_bwd.restype = ctypes.c_int
         lib.attn_bwd_workspace_size.argtypes = [ctypes.c_int] * 3
         lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
+        lib.attn_quantize_fp8.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + [
+            ctypes.c_void_p]
+        lib.attn_quantize_fp8.restype = ctypes.c_int
+        lib.attn_fwd_fp8.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int] * 4 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+        lib.attn_fwd_fp8.restype = ctypes.c_int
         lib.attn_status_string.argtypes = [ctypes.c_int]
         lib.attn_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -206,3 +212,67 @@ def attn_bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = Fal
     if st != TA_OK:
         raise RuntimeError("attn_bwd failed: %s (status %d)" % (attn_status_string(st), st))
     return dq, dk, dv
+
+
+def attn_quantize_fp8(x, out=None, descale=None, stream=None):
+    """Per-head FP8 (OCP E4M3) codes of a bf16 device tensor [..., rows, d].
+
+    Returns (codes uint8 tensor of x's shape, descale float32 tensor of shape
+    x.shape[:-2]) with x ~= e4m3(codes) * descale.
+    """
+    import torch
+    lib = load_library()
+    if not x.is_cuda or x.dtype != torch.bfloat16 or x.dim() < 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bfloat16 device tensor [..., rows, d]")
+    rows, d = int(x.shape[-2]), int(x.shape[-1])
+    heads = x.numel() // max(rows * d, 1)
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if descale is None:
+        descale = torch.empty(x.shape[:-2], dtype=torch.float32, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    st = lib.attn_quantize_fp8(x.data_ptr(), out.data_ptr(), descale.data_ptr(), heads, rows, d,
+                               int(stream))
+    if st != TA_OK:
+        raise RuntimeError("attn_quantize_fp8 failed: %s (status %d)" % (attn_status_string(st), st))
+    return out, descale
+
+
+def attn_fwd_fp8_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, qd_ptr, kd_ptr, B, H, N, d, scale,
+                     causal, stream=0) -> int:
+    return load_library().attn_fwd_fp8(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, qd_ptr, kd_ptr, B, H,
+                                       N, d, ctypes.c_float(scale), causal, stream)
+
+
+def attn_fwd_fp8(q8, k8, v, q_descale, k_descale, scale: float | None = None, causal=False,
+                 out=None, lse=None, stream=None):
+    """Attention forward with FP8 scores: q8, k8 uint8 E4M3 codes [B, H, N, d]
+    (from attn_quantize_fp8), v bf16 [B, H, N, d], descales float32 [B, H]."""
+    import torch
+    lib = load_library()
+    if q8.dtype != torch.uint8 or k8.dtype != torch.uint8 or v.dtype != torch.bfloat16:
+        raise ValueError("q8, k8 must be uint8 codes and v bfloat16")
+    if q8.dim() != 4 or q8.shape != k8.shape or q8.shape != v.shape:
+        raise ValueError("q8, k8, v must share one shape [B, H, N, d]")
+    for t in (q8, k8, v, q_descale, k_descale):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("inputs must be contiguous device tensors")
+    B, H, N, d = (int(x) for x in q8.shape)
+    if tuple(q_descale.shape) != (B, H) or tuple(k_descale.shape) != (B, H) \
+            or q_descale.dtype != torch.float32 or k_descale.dtype != torch.float32:
+        raise ValueError("descales must be float32 [B, H]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.float32, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q8.device).cuda_stream
+    st = lib.attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v.data_ptr(), out.data_ptr(),
+                          lse.data_ptr(), q_descale.data_ptr(), k_descale.data_ptr(), B, H, N, d,
+                          ctypes.c_float(float(scale)), int(bool(causal)), int(stream))
+    if st != TA_OK:
+        raise RuntimeError("attn_fwd_fp8 failed: %s (status %d)" % (attn_status_string(st), st))
+    return out, lse

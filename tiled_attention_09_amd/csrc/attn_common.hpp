@@ -21,6 +21,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
 constexpr int kWaves = 4;
@@ -250,6 +251,26 @@ struct LdsReader {
     }
     return __builtin_bit_cast(bf16x8,
                               __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+};
+
+// A operands of the FP8 score product (v_mfma_scale_f32_32x32x64_f8f6f4) from
+// a tile of 128-byte rows (128 FP8 values; the geometry and swizzle of a bf16
+// Tile<64>): row 32 rb + l32, bytes [64 ks + 32 hi, +32) as two 16-byte reads.
+// Both operands of the product use this byte order, so the k order inside the
+// instruction does not matter.  Chunk indices 4 ks + 2 hi + part have disjoint
+// bits, so the swizzle is one per-lane XOR with a compile-time constant.
+struct LdsReaderF8 {
+  uint32_t rows;
+  __device__ __forceinline__ explicit LdsReaderF8(int lane) {
+    const int l32 = lane & 31, hi = lane >> 5;
+    rows = (uint32_t)(l32 * 128) | ((uint32_t)((2 * hi) ^ Tile<64>::swz(l32)) << 4);
+  }
+  __device__ __forceinline__ i32x8 row_op(const TA_LDS uint8_t* t, int rb, int ks) const {
+    const TA_LDS char* base = (const TA_LDS char*)t + rb * 32 * 128;
+    const u32x4 a = *reinterpret_cast<const TA_LDS u32x4*>(base + (rows ^ (uint32_t)((4 * ks) << 4)));
+    const u32x4 b = *reinterpret_cast<const TA_LDS u32x4*>(base + (rows ^ (uint32_t)((4 * ks + 1) << 4)));
+    return __builtin_bit_cast(i32x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
   }
 };
 

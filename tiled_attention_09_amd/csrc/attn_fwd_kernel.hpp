@@ -59,21 +59,32 @@ constexpr int kValuPerMfma = 7;
 // absolute positions offset .. offset + Nq - 1 attend Nk keys at positions
 // 0 .. Nk - 1 (causal: key j visible to query i iff j <= i + offset).
 // GENERAL = false is the square case (Nk = Nq, offset 0) with those facts
-// known at compile time.
-template <int D, int DV, bool CAUSAL, bool POS_SCALE, bool GENERAL>
+// known at compile time.  F8: Q and K are FP8 (OCP E4M3) codes with per-head
+// descale factors (Q = codes * q_descale[b h], likewise K), the scores use the
+// FP8 matrix product, and the descales fold into the exponent scale (d = 128,
+// square shapes).
+template <int D, int DV, bool CAUSAL, bool POS_SCALE, bool GENERAL, bool F8 = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
                      const uint16_t* __restrict__ V, float* __restrict__ O,
                      float* __restrict__ LSE, int bh_count, int Nq, int nk_arg, int offset_arg,
-                     int n_qt, float scale_log2) {
+                     int n_qt, float scale_log2, const float* __restrict__ q_descale,
+                     const float* __restrict__ k_descale) {
+  static_assert(!F8 || (D == 128 && DV == 128 && !GENERAL), "FP8 scores: d = 128, square");
   const int Nk = GENERAL ? nk_arg : Nq;
   const int offset = GENERAL ? offset_arg : 0;
   using T = Tile<D>;
   using TV = Tile<DV>;
-  __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[kBN * D];
+  // K tile geometry in bytes: an FP8 row of 128 values is laid out like a
+  // bf16 row of 64 (128 bytes, 8 chunks).
+  using TK = Tile<F8 ? 64 : D>;
+  constexpr uint32_t kElemQK = F8 ? 1u : 2u;     // bytes per Q / K value
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[TK::BYTES];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[kBN * DV];
-  __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[TK::BYTES];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[kBN * DV];
+  const char* Q = static_cast<const char*>(Qv);
+  const char* K = static_cast<const char*>(Kv);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -84,26 +95,43 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   int bh, qt;
   map_block(blockIdx.x, bh_count, n_qt, CAUSAL, bh, qt);
 
-  const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + (size_t)bh * Nq * D, (uint32_t)Nq * D * 2u);
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + (size_t)bh * Nk * D, (uint32_t)Nk * D * 2u);
+  const __amdgpu_buffer_rsrc_t qr =
+      make_rsrc(Q + (size_t)bh * Nq * D * kElemQK, (uint32_t)Nq * D * kElemQK);
+  const __amdgpu_buffer_rsrc_t kr =
+      make_rsrc(K + (size_t)bh * Nk * D * kElemQK, (uint32_t)Nk * D * kElemQK);
+  if constexpr (F8) scale_log2 *= q_descale[bh] * k_descale[bh];   // online descaling
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + (size_t)bh * Nk * DV, (uint32_t)Nk * DV * 2u);
 
   const int q0 = qt * kBM + wave * 32;   // first query row of this wave
   const int my_q = q0 + l32;             // this lane's query row
 
-  // Q fragment (B operand of S^T = K Q^T): Q[my_q][16 ks + 8 hi + 0..7].
-  bf16x8 qf[T::KS];
+  // Q fragment (B operand of S^T = K Q^T): bf16 Q[my_q][16 ks + 8 hi + 0..7];
+  // FP8: bytes [64 ks + 32 hi, +32) of row my_q (the byte order of the K reads).
+  constexpr int KS8 = D / 64;
+  bf16x8 qf[F8 ? 1 : T::KS];
+  i32x8 qf8[F8 ? KS8 : 1];
+  if constexpr (F8) {
 #pragma unroll
-  for (int ks = 0; ks < T::KS; ++ks)
-    qf[ks] = __builtin_bit_cast(bf16x8, load16(qr, (uint32_t)(my_q * D + 16 * ks + 8 * hi) * 2u));
+    for (int ks = 0; ks < KS8; ++ks) {
+      const uint32_t off = (uint32_t)(my_q * D + 64 * ks + 32 * hi);
+      qf8[ks] = __builtin_bit_cast(
+          i32x8, __builtin_shufflevector(load16(qr, off), load16(qr, off + 16u), 0, 1, 2, 3, 4, 5,
+                                         6, 7));
+    }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks)
+      qf[ks] = __builtin_bit_cast(bf16x8, load16(qr, (uint32_t)(my_q * D + 16 * ks + 8 * hi) * 2u));
+  }
 
   // Tile copy offsets: the same for every tile (K and V differ only when D != DV).
-  uint32_t src_k[T::LOADS], src_v[TV::LOADS];
-  tile_src_offsets<D>(src_k, wave, lane);
+  uint32_t src_k[TK::LOADS], src_v[TV::LOADS];
+  tile_src_offsets<F8 ? 64 : D>(src_k, wave, lane);
   tile_src_offsets<DV>(src_v, wave, lane);
   // Operand reads: K row-wise (A operand of S^T), V transposed (A operand of
   // O^T), with lane offsets whose row/stage parts fold into the instruction.
   const LdsReader<D> rd(lane);
+  const LdsReaderF8 rd8(lane);
   const LdsReader<DV> rdv(lane);
 
   f32x16 oacc[TV::DB];
@@ -127,18 +155,32 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 
   // S^T (64 keys x 32 queries) of the key tile in `kt`: block kb covers tile
   // keys 32 kb + [0, 32).
-  auto scores = [&](const TA_LDS uint16_t* kt, f32x16 (&s)[2]) __attribute__((always_inline)) {
+  auto scores = [&](const TA_LDS uint8_t* kt, f32x16 (&s)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+    if constexpr (F8) {
+      // 32x32x64 FP8 products (unit block scales: exponent 127 = 2^0).
 #pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks)
+      for (int ks = 0; ks < KS8; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd.row_op(kt, kb, ks), qf[ks], s[kb], 0, 0,
-                                                        0);
+        for (int kb = 0; kb < 2; ++kb)
+          s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(rd8.row_op(kt, kb, ks), qf8[ks],
+                                                                  s[kb], 0, 0, 0, 127, 0, 127);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < T::KS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              rd.row_op((const TA_LDS uint16_t*)kt, kb, ks), qf[ks], s[kb], 0, 0, 0);
+    }
   };
+  // Score products per tile and the LDS reads that feed them.
+  constexpr int kScoreMfma = F8 ? 2 * KS8 : 2 * T::KS;
+  constexpr int kScoreReads = F8 ? 2 * kScoreMfma : kScoreMfma;
+  constexpr int kValuPerScore = F8 ? 4 * kValuPerMfma : kValuPerMfma;
 
   // Scale (non-positive scales only) and hide future / non-existent keys of key
   // tile j in s; only tiles crossing the diagonal or the end of the keys need
@@ -215,14 +257,14 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   // also frees K_j's and V_{j-1}'s stages, which receive K_{j+2} and V_{j+1}.
   // Each iteration: S_{j+1} = K_{j+1} Q^T interleaved with the softmax of S_j,
   // the alpha rescale of o (only when some row moved its maximum), then P_j V_j.
-  TA_LDS uint16_t* const k0 = (TA_LDS uint16_t*)k_lds0;
+  TA_LDS uint8_t* const k0 = (TA_LDS uint8_t*)k_lds0;
   TA_LDS uint16_t* const v0 = (TA_LDS uint16_t*)v_lds0;
-  TA_LDS uint16_t* const k1 = (TA_LDS uint16_t*)k_lds1;
+  TA_LDS uint8_t* const k1 = (TA_LDS uint8_t*)k_lds1;
   TA_LDS uint16_t* const v1 = (TA_LDS uint16_t*)v_lds1;
   f32x16 sa[2], sb[2];
   bf16x8 pf[4];
 
-  auto step = [&](int j, const TA_LDS uint16_t* k_next, const TA_LDS uint16_t* v_cur,
+  auto step = [&](int j, const TA_LDS uint8_t* k_next, const TA_LDS uint16_t* v_cur,
                   f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) __attribute__((always_inline)) {
     prepare(j, s_cur);
     // S_{j+1} is computed even when this wave has no tile j+1 (its last tile):
@@ -235,8 +277,9 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     // Issue order: four K operand reads ahead, then each product followed by
     // one read and a share of the softmax's vector instructions.
     sched_reads<4>();
-    sched_rep<1, kValuPerMfma, 2 * T::KS - 4>();
-    sched_rep<0, kValuPerMfma, 4>();
+    sched_rep<(kScoreReads - 4) / (kScoreMfma - 4 > 0 ? kScoreMfma - 4 : kScoreMfma), kValuPerScore,
+              (kScoreMfma - 4 > 0 ? kScoreMfma - 4 : kScoreMfma)>();
+    sched_rep<0, kValuPerScore, (kScoreMfma - 4 > 0 ? 4 : 0)>();
     // The probabilities must be complete here, inside the region shared with
     // the score products: without this use the compiler sinks the
     // exponentials below the rescale branch, out of reach of the interleave.
@@ -255,7 +298,8 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     constexpr int P = decltype(pc)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();                 // K_{j+1}, V_j visible; K_j, V_{j-1} stages free
-    if (j + 2 < n_kt) issue_rows<D>(kr, src_k, j + 2, wave, P ? k1 : k0);
+    if (j + 2 < n_kt)
+      issue_rows<F8 ? 64 : D>(kr, src_k, j + 2, wave, (TA_LDS uint16_t*)(P ? k1 : k0));
     if (j + 1 < n_kt) issue_rows<DV>(vr, src_v, j + 1, wave, P ? v0 : v1);
     if (j < n_w) {
       if constexpr (P == 0)
@@ -266,9 +310,9 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   };
 
   if (n_kt > 0) {
-    issue_rows<D>(kr, src_k, 0, wave, k0);
+    issue_rows<F8 ? 64 : D>(kr, src_k, 0, wave, (TA_LDS uint16_t*)k0);
     issue_rows<DV>(vr, src_v, 0, wave, v0);
-    if (n_kt > 1) issue_rows<D>(kr, src_k, 1, wave, k1);
+    if (n_kt > 1) issue_rows<F8 ? 64 : D>(kr, src_k, 1, wave, (TA_LDS uint16_t*)k1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (n_w > 0) scores(k0, sa);
