@@ -180,7 +180,7 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
   // Score products per tile and the LDS reads that feed them.
   constexpr int kScoreMfma = F8 ? 2 * KS8 : 2 * T::KS;
   constexpr int kScoreReads = F8 ? 2 * kScoreMfma : kScoreMfma;
-  constexpr int kValuPerScore = F8 ? 4 * kValuPerMfma : kValuPerMfma;
+  constexpr int kValuPerScore = F8 ? 16 : kValuPerMfma;
 
   // Scale (non-positive scales only) and hide future / non-existent keys of key
   // tile j in s; only tiles crossing the diagonal or the end of the keys need
