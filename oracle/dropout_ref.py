@@ -1,0 +1,106 @@
+"""Attention with dropout on the probabilities -- oracle side.
+
+TEST INFRASTRUCTURE ONLY (tests, the smoke check and the benchmark's CPU leg
+may use it; nothing is shared with the HIP path).
+
+Page "22. GPU Engineering: Correctness, Throughput, and Attention", sec. 22.5:
+dropout is to be added only after the masks are defined reproducibly.  The
+definition used here (this library's reading; the pages give none):
+
+* Generator: Philox-4x64 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel
+  random numbers: as easy as 1, 2, 3", SC 2011): a 256-bit counter (four
+  64-bit words) and a 128-bit key (two words); each round multiplies words 0
+  and 2 by fixed odd constants into 128-bit products and mixes their halves
+  with words 1 and 3 and the key; the key is advanced by two Weyl constants
+  between rounds.
+* Mask: for head n = b*H + h, query row i and key j,
+      word = Philox(counter = (i, j >> 5, n, 0), key = (seed, 0))
+      byte = bits 8 (j mod 8) .. +7 of word[(j >> 3) mod 4]   (byte j mod 32, little endian)
+      keep(i, j) = byte >= t,    drop probability t / 256,  t in 0..255.
+* Output: O = (P * M) V / (1 - t/256) with P the softmax of the scaled, masked
+  scores (the normaliser counts every visible key, kept or dropped); LSE is the
+  undropped log-normaliser.  t = 0 keeps everything and is plain attention.
+* Gradients (the chain rule through the mask): with Pd = P * M / (1 - t/256),
+  dV = Pd^T G, dP = (G V^T) * M / (1 - t/256), dS = P * (dP - rowsum(dP * P)),
+  dQ = scale dS K, dK = scale dS^T Q; rowsum(dP * P) still equals
+  rowsum(G * O) (the sec. 22.7 identity applied to O = Pd V).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention_ref import _visible
+
+__all__ = ["philox4x64", "dropout_keep", "attention_dropout_ref", "attention_dropout_bwd_ref"]
+
+_M0 = 0xD2E7470EE14C6C93
+_M1 = 0xCA5A826395121157
+_W0 = 0x9E3779B97F4A7C15
+_W1 = 0xBB67AE8584CAA73B
+_MASK64 = (1 << 64) - 1
+
+
+def philox4x64(counter, key, rounds: int = 10):
+    """Philox-4x64 block for one counter (4 ints) and key (2 ints): 4 ints."""
+    x0, x1, x2, x3 = (int(c) & _MASK64 for c in counter)
+    k0, k1 = (int(k) & _MASK64 for k in key)
+    for r in range(rounds):
+        if r:
+            k0 = (k0 + _W0) & _MASK64
+            k1 = (k1 + _W1) & _MASK64
+        p0 = _M0 * x0
+        p1 = _M1 * x2
+        hi0, lo0 = p0 >> 64, p0 & _MASK64
+        hi1, lo1 = p1 >> 64, p1 & _MASK64
+        x0, x1, x2, x3 = hi1 ^ x1 ^ k0, lo1, hi0 ^ x3 ^ k1, lo0
+    return x0, x1, x2, x3
+
+
+def dropout_keep(n_head: int, rows, nk: int, seed: int, t: int) -> np.ndarray:
+    """Boolean keep mask [len(rows), nk] of head n_head (flat b*H + h)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    keep = np.ones((rows.size, nk), dtype=bool)
+    if t == 0:
+        return keep
+    for a, i in enumerate(rows):
+        for blk in range((nk + 31) // 32):
+            w = philox4x64((int(i), blk, n_head, 0), (seed, 0))
+            for jj in range(32):
+                j = blk * 32 + jj
+                if j >= nk:
+                    break
+                byte = (w[jj >> 3] >> (8 * (jj & 7))) & 0xFF
+                keep[a, j] = byte >= t
+    return keep
+
+
+def _probs(q, k, scale, causal, rows):
+    s = float(scale) * (q[rows] @ k.T)
+    s = np.where(_visible(q.shape[0], k.shape[0], causal, 0, rows), s, -np.inf)
+    m = s.max(axis=1)
+    p = np.exp(s - m[:, None])
+    l = p.sum(axis=1)
+    return p / l[:, None], m + np.log(l)
+
+
+def attention_dropout_ref(q, k, v, scale: float, causal: bool, n_head: int, seed: int, t: int,
+                          rows=None):
+    """One head: (O [R, dv], LSE [R]) with the dropout mask above, float64."""
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    p, lse = _probs(q, k, scale, causal, rows)
+    keep = dropout_keep(n_head, rows, k.shape[0], seed, t)
+    return (p * keep) @ v / (1.0 - t / 256.0), lse
+
+
+def attention_dropout_bwd_ref(q, k, v, do, scale: float, causal: bool, n_head: int, seed: int,
+                              t: int):
+    """One head: (dQ, dK, dV) of sum(G * O) with O from attention_dropout_ref."""
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    rows = np.arange(q.shape[0])
+    p, _ = _probs(q, k, scale, causal, rows)
+    mk = dropout_keep(n_head, rows, k.shape[0], seed, t) / (1.0 - t / 256.0)
+    dv = (p * mk).T @ do
+    dp = (do @ v.T) * mk
+    ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))
+    return float(scale) * (ds @ k), float(scale) * (ds.T @ q), dv
