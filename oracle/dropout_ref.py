@@ -7,15 +7,17 @@ Page "22. GPU Engineering: Correctness, Throughput, and Attention", sec. 22.5:
 dropout is to be added only after the masks are defined reproducibly.  The
 definition used here (this library's reading; the pages give none):
 
-* Generator: Philox-4x64 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel
-  random numbers: as easy as 1, 2, 3", SC 2011): a 256-bit counter (four
-  64-bit words) and a 128-bit key (two words); each round multiplies words 0
-  and 2 by fixed odd constants into 128-bit products and mixes their halves
+* Generator: Philox-4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel
+  random numbers: as easy as 1, 2, 3", SC 2011): a 128-bit counter (four
+  32-bit words) and a 64-bit key (two words); each round multiplies words 0
+  and 2 by fixed odd constants into 64-bit products and mixes their halves
   with words 1 and 3 and the key; the key is advanced by two Weyl constants
-  between rounds.
+  between rounds.  (32-bit words: one block is 16 random bytes for about 80
+  32-bit vector operations on the GPU; the 64-bit variant needs emulated
+  128-bit products.)
 * Mask: for head n = b*H + h, query row i and key j,
-      word = Philox(counter = (i, j >> 5, n, 0), key = (seed, 0))
-      byte = bits 8 (j mod 8) .. +7 of word[(j >> 3) mod 4]   (byte j mod 32, little endian)
+      word = Philox(counter = (i, j >> 4, n, 0), key = (seed mod 2^32, seed >> 32))
+      byte = bits 8 (j mod 4) .. +7 of word[(j >> 2) mod 4]   (byte j mod 16, little endian)
       keep(i, j) = byte >= t,    drop probability t / 256,  t in 0..255.
 * Output: O = (P * M) V / (1 - t/256) with P the softmax of the scaled, masked
   scores (the normaliser counts every visible key, kept or dropped); LSE is the
@@ -31,27 +33,27 @@ import numpy as np
 
 from .attention_ref import _visible
 
-__all__ = ["philox4x64", "dropout_keep", "attention_dropout_ref", "attention_dropout_bwd_ref"]
+__all__ = ["philox4x32", "dropout_keep", "attention_dropout_ref", "attention_dropout_bwd_ref"]
 
-_M0 = 0xD2E7470EE14C6C93
-_M1 = 0xCA5A826395121157
-_W0 = 0x9E3779B97F4A7C15
-_W1 = 0xBB67AE8584CAA73B
-_MASK64 = (1 << 64) - 1
+_M0 = 0xD2511F53
+_M1 = 0xCD9E8D57
+_W0 = 0x9E3779B9
+_W1 = 0xBB67AE85
+_MASK32 = 0xFFFFFFFF
 
 
-def philox4x64(counter, key, rounds: int = 10):
-    """Philox-4x64 block for one counter (4 ints) and key (2 ints): 4 ints."""
-    x0, x1, x2, x3 = (int(c) & _MASK64 for c in counter)
-    k0, k1 = (int(k) & _MASK64 for k in key)
+def philox4x32(counter, key, rounds: int = 10):
+    """Philox-4x32 block for one counter (4 ints) and key (2 ints): 4 ints."""
+    x0, x1, x2, x3 = (int(c) & _MASK32 for c in counter)
+    k0, k1 = (int(k) & _MASK32 for k in key)
     for r in range(rounds):
         if r:
-            k0 = (k0 + _W0) & _MASK64
-            k1 = (k1 + _W1) & _MASK64
+            k0 = (k0 + _W0) & _MASK32
+            k1 = (k1 + _W1) & _MASK32
         p0 = _M0 * x0
         p1 = _M1 * x2
-        hi0, lo0 = p0 >> 64, p0 & _MASK64
-        hi1, lo1 = p1 >> 64, p1 & _MASK64
+        hi0, lo0 = p0 >> 32, p0 & _MASK32
+        hi1, lo1 = p1 >> 32, p1 & _MASK32
         x0, x1, x2, x3 = hi1 ^ x1 ^ k0, lo1, hi0 ^ x3 ^ k1, lo0
     return x0, x1, x2, x3
 
@@ -62,14 +64,15 @@ def dropout_keep(n_head: int, rows, nk: int, seed: int, t: int) -> np.ndarray:
     keep = np.ones((rows.size, nk), dtype=bool)
     if t == 0:
         return keep
+    key = (seed & _MASK32, (seed >> 32) & _MASK32)
     for a, i in enumerate(rows):
-        for blk in range((nk + 31) // 32):
-            w = philox4x64((int(i), blk, n_head, 0), (seed, 0))
-            for jj in range(32):
-                j = blk * 32 + jj
+        for blk in range((nk + 15) // 16):
+            w = philox4x32((int(i), blk, n_head, 0), key)
+            for jj in range(16):
+                j = blk * 16 + jj
                 if j >= nk:
                     break
-                byte = (w[jj >> 3] >> (8 * (jj & 7))) & 0xFF
+                byte = (w[jj >> 2] >> (8 * (jj & 3))) & 0xFF
                 keep[a, j] = byte >= t
     return keep
 

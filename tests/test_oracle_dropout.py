@@ -1,44 +1,51 @@
-"""CPU pins of the dropout oracle: the Philox-4x64-10 generator against numpy's
-independent implementation, the mask statistics, t = 0 reducing to plain
-attention, and the gradients through the mask against finite differences and
-torch float64 autograd."""
+"""CPU pins of the dropout oracle: the Philox-4x32-10 generator against the
+published known-answer vectors, the byte order of the mask, the mask
+statistics, t = 0 reducing to plain attention, and the gradients through the
+mask against finite differences and torch float64 autograd."""
 from __future__ import annotations
+
+import json
+import os
 
 import numpy as np
 import pytest
 import torch
 
 from oracle import (attention_bwd_ref, attention_dropout_bwd_ref, attention_dropout_ref,
-                    attention_ref, dropout_keep, philox4x64)
+                    attention_ref, dropout_keep, philox4x32)
+
+_KAT = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "philox4x32_10_kat.json")))
 
 
-def _numpy_philox(counter, key):
-    """numpy's Philox-4x64-10: the state counter is advanced (256-bit, with
-    carry) before each block, so start one below the wanted counter."""
-    c = sum(int(w) << (64 * i) for i, w in enumerate(counter))
-    c = (c - 1) % (1 << 256)
-    words = np.array([(c >> (64 * i)) & ((1 << 64) - 1) for i in range(4)], dtype=np.uint64)
-    bg = np.random.Philox(counter=words, key=np.array(key, dtype=np.uint64))
-    return tuple(int(x) for x in bg.random_raw(4))
+def _hex(words):
+    return tuple(int(w, 16) for w in words)
 
 
-@pytest.mark.parametrize("counter,key", [
-    ((0, 0, 0, 0), (0, 0)),
-    ((1, 2, 3, 4), (5, 7)),
-    ((8191, 255, 63, 0), (123456789, 0)),
-    ((0, 1, 0, 0), (2 ** 64 - 1, 2 ** 63)),          # numpy's start needs a borrow
-    ((2 ** 64 - 1, 2 ** 64 - 1, 2 ** 64 - 1, 2 ** 64 - 1), (3, 4)),
-])
-def test_philox_matches_numpy(counter, key):
-    assert philox4x64(counter, key) == _numpy_philox(counter, key)
+@pytest.mark.parametrize("i", range(len(_KAT["vectors"])))
+def test_philox_known_answers(i):
+    v = _KAT["vectors"][i]
+    assert philox4x32(_hex(v["counter"]), _hex(v["key"])) == _hex(v["out"])
 
 
-def test_philox_random_counters_match_numpy():
-    rng = np.random.default_rng(7)
-    for _ in range(50):
-        c = tuple(int(x) for x in rng.integers(0, 2 ** 63, 4))
-        k = tuple(int(x) for x in rng.integers(0, 2 ** 63, 2))
-        assert philox4x64(c, k) == _numpy_philox(c, k)
+def test_philox_known_answers_reject_other_round_counts():
+    v = _KAT["vectors"][2]
+    for rounds in (7, 9, 11):
+        assert philox4x32(_hex(v["counter"]), _hex(v["key"]), rounds) != _hex(v["out"])
+
+
+def test_mask_bytes_are_the_little_endian_block():
+    """keep[i, j] is byte j mod 16 of the block (row i, j // 16, head, 0) laid
+    out as four little-endian 32-bit words; the seed's low word is key word 0."""
+    seed, head, t = (7 << 32) | 12345, 5, 100
+    rows, nk = np.array([0, 3, 70000]), 45
+    keep = dropout_keep(head, rows, nk, seed, t)
+    for a, i in enumerate(rows):
+        for blk in range(3):
+            raw = np.array(philox4x32((int(i), blk, head, 0), (12345, 7)), dtype="<u4").tobytes()
+            for jj in range(16):
+                j = 16 * blk + jj
+                if j < nk:
+                    assert keep[a, j] == (raw[jj] >= t)
 
 
 @pytest.mark.parametrize("t", [1, 64, 128, 230])
