@@ -24,6 +24,7 @@
 #define TILEDATTN_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -140,6 +141,33 @@ int attn_quantize_fp8(const void* x, void* out, float* descale, int heads, int r
 int attn_fwd_fp8(const void* q8, const void* k8, const void* v, float* o, float* lse,
                  const float* q_descale, const float* k_descale, int B, int H, int N, int d,
                  float scale, int causal, void* stream);
+
+/*
+ * attn_fwd_dropout -- attn_fwd with dropout on the probabilities (page
+ * "22. GPU Engineering: Correctness, Throughput, and Attention", sec. 22.5:
+ * dropout only with reproducible masks).  For head n = b * H + h, query row i
+ * and key j the mask byte is
+ *
+ *     byte(i, j) = byte (j mod 16) of Philox-4x32-10(counter = (i, j / 16, n, 0),
+ *                                                    key = (seed mod 2^32, seed / 2^32))
+ *
+ * (the generator's four 32-bit output words read as 16 little-endian bytes;
+ * Salmon, Moraes, Dror, Shaw, SC 2011), P[i, j] is kept when byte >= drop_t,
+ * and
+ *
+ *     O[i,:] = 256 / (256 - drop_t) * sum_j keep(i, j) softmax_j(S[i,:]) v_j
+ *     LSE[i] = ln sum_j exp(S[i,j])         (every visible key, kept or not)
+ *
+ * so the drop probability is drop_t / 256 and drop_t = 0 is attn_fwd.  The
+ * mask is a pure function of (seed, n, i, j): attn_bwd_dropout regenerates it.
+ *
+ *   seed   : any 64-bit value.
+ *   drop_t : 0 .. 255 (TA_ERR_INVALID_ARG otherwise).
+ *   q, k, v, o, lse, B, H, N, d, scale, causal, stream, errors: as for attn_fwd.
+ */
+int attn_fwd_dropout(const void* q, const void* k, const void* v, float* o, float* lse, int B,
+                     int H, int N, int d, float scale, int causal, uint64_t seed, int drop_t,
+                     void* stream);
 
 /*
  * attn_bwd_workspace_size -- bytes of device workspace attn_bwd needs for

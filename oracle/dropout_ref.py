@@ -58,23 +58,36 @@ def philox4x32(counter, key, rounds: int = 10):
     return x0, x1, x2, x3
 
 
+def _philox4x32_arrays(x0, x1, x2, x3, k0: int, k1: int, rounds: int = 10):
+    """philox4x32 over broadcast numpy counter words (uint64 arrays holding
+    32-bit values, so each 32 x 32-bit product is exact)."""
+    x0, x1, x2, x3 = (np.asarray(x, dtype=np.uint64) & np.uint64(_MASK32) for x in (x0, x1, x2, x3))
+    x0, x1, x2, x3 = np.broadcast_arrays(x0, x1, x2, x3)
+    for r in range(rounds):
+        if r:
+            k0 = (k0 + _W0) & _MASK32
+            k1 = (k1 + _W1) & _MASK32
+        p0 = np.uint64(_M0) * x0
+        p1 = np.uint64(_M1) * x2
+        hi0, lo0 = p0 >> np.uint64(32), p0 & np.uint64(_MASK32)
+        hi1, lo1 = p1 >> np.uint64(32), p1 & np.uint64(_MASK32)
+        x0, x1, x2, x3 = hi1 ^ x1 ^ np.uint64(k0), lo1, hi0 ^ x3 ^ np.uint64(k1), lo0
+    return x0, x1, x2, x3
+
+
 def dropout_keep(n_head: int, rows, nk: int, seed: int, t: int) -> np.ndarray:
-    """Boolean keep mask [len(rows), nk] of head n_head (flat b*H + h)."""
+    """Boolean keep mask [len(rows), nk] of head n_head (flat b*H + h): the
+    blocks for counters (row, block, n_head, 0), block = 0 .. ceil(nk/16) - 1,
+    evaluated as arrays, each block's four words read as 16 little-endian bytes."""
     rows = np.asarray(rows, dtype=np.int64)
-    keep = np.ones((rows.size, nk), dtype=bool)
-    if t == 0:
-        return keep
-    key = (seed & _MASK32, (seed >> 32) & _MASK32)
-    for a, i in enumerate(rows):
-        for blk in range((nk + 15) // 16):
-            w = philox4x32((int(i), blk, n_head, 0), key)
-            for jj in range(16):
-                j = blk * 16 + jj
-                if j >= nk:
-                    break
-                byte = (w[jj >> 2] >> (8 * (jj & 3))) & 0xFF
-                keep[a, j] = byte >= t
-    return keep
+    if t == 0 or rows.size == 0 or nk == 0:
+        return np.ones((rows.size, nk), dtype=bool)
+    nb = (nk + 15) // 16
+    words = _philox4x32_arrays(rows[:, None], np.arange(nb)[None, :], n_head, 0,
+                               seed & _MASK32, (seed >> 32) & _MASK32)
+    block = np.stack(words, axis=-1).astype("<u4")                  # [R, nb, 4]
+    raw = block.view(np.uint8).reshape(rows.size, nb * 16)[:, :nk]  # byte j of the row
+    return raw >= t
 
 
 def _probs(q, k, scale, causal, rows):

@@ -41,8 +41,8 @@ def declared_functions():
 
 def test_header_declares_entry_points():
     assert declared_functions() == ["attn_bwd", "attn_bwd_workspace_size", "attn_fwd",
-                                    "attn_fwd_ex", "attn_fwd_fp8", "attn_quantize_fp8",
-                                    "attn_status_string"]
+                                    "attn_fwd_dropout", "attn_fwd_ex", "attn_fwd_fp8",
+                                    "attn_quantize_fp8", "attn_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -268,3 +268,32 @@ def test_quantize_validation():
     assert q(d=96) == ta.TA_ERR_UNSUPPORTED
     assert q(o=A + 8) == ta.TA_ERR_MISALIGNED
     assert q(dsc=A + 2) == ta.TA_ERR_MISALIGNED
+
+
+# ---- dropout entry points -------------------------------------------------------
+
+def call_drop(**over):
+    args = dict(q=A, k=A, v=A, o=A, lse=A, B=1, H=2, N=256, d=128, scale=0.09, causal=1,
+                seed=12345, t=64)
+    args.update(over)
+    return ta.attn_fwd_dropout_raw(args["q"], args["k"], args["v"], args["o"], args["lse"],
+                                   args["B"], args["H"], args["N"], args["d"], args["scale"],
+                                   args["causal"], args["seed"], args["t"], 0)
+
+
+@host_only
+@pytest.mark.parametrize("over", [dict(q=0), dict(lse=0), dict(N=0), dict(B=0), dict(causal=2),
+                                  dict(scale=math.nan), dict(t=-1), dict(t=256)])
+def test_dropout_fwd_invalid(over):
+    assert call_drop(**over) == ta.TA_ERR_INVALID_ARG
+
+
+@host_only
+def test_dropout_fwd_head_dims():
+    assert call_drop(d=96) == ta.TA_ERR_UNSUPPORTED
+
+
+@host_only
+@pytest.mark.parametrize("field,off", [("q", 8), ("v", 4), ("o", 8), ("lse", 2)])
+def test_dropout_fwd_misaligned(field, off):
+    assert call_drop(**{field: A + off}) == ta.TA_ERR_MISALIGNED

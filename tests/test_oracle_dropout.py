@@ -48,6 +48,22 @@ def test_mask_bytes_are_the_little_endian_block():
                     assert keep[a, j] == (raw[jj] >= t)
 
 
+def test_mask_matches_scalar_generator_on_random_positions():
+    """The array evaluation of dropout_keep against one scalar block per element."""
+    rng = np.random.default_rng(21)
+    for _ in range(3):
+        seed = int(rng.integers(0, 2 ** 63)) * 2 + 1
+        head, t = int(rng.integers(0, 2 ** 31)), int(rng.integers(1, 256))
+        rows = rng.integers(0, 2 ** 31, 5)
+        nk = int(rng.integers(1, 300))
+        keep = dropout_keep(head, rows, nk, seed, t)
+        for a, i in enumerate(rows):
+            for j in rng.integers(0, nk, 20):
+                w = philox4x32((int(i), int(j) >> 4, head, 0), (seed & 0xFFFFFFFF, seed >> 32))
+                byte = (w[(int(j) >> 2) & 3] >> (8 * (int(j) & 3))) & 0xFF
+                assert keep[a, j] == (byte >= t)
+
+
 @pytest.mark.parametrize("t", [1, 64, 128, 230])
 def test_keep_fraction(t):
     keep = dropout_keep(3, np.arange(200), 500, seed=11, t=t)

@@ -48,6 +48,9 @@ def load_library() -> ctypes.CDLL:
         lib.attn_fwd_fp8.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int] * 4 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
         lib.attn_fwd_fp8.restype = ctypes.c_int
+        lib.attn_fwd_dropout.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p]
+        lib.attn_fwd_dropout.restype = ctypes.c_int
         lib.attn_status_string.argtypes = [ctypes.c_int]
         lib.attn_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -100,6 +103,61 @@ def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None
                       B, H, N, d, ctypes.c_float(float(scale)), int(bool(causal)), int(stream))
     if st != TA_OK:
         raise RuntimeError("attn_fwd failed: %s (status %d)" % (attn_status_string(st), st))
+    return out, lse
+
+
+def _fwd_buffers(q, k, v, out, lse):
+    """Checks of the square forward's inputs; returns (B, H, N, d, out, lse)."""
+    import torch
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise ValueError("q, k, v must be bfloat16")
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one shape [B, H, N, d]")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, N, d = (int(x) for x in q.shape)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out.shape != (B, H, N, d) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be contiguous float32 [B, H, N, d]")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    return B, H, N, d, out, lse
+
+
+def attn_fwd_dropout_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int,
+                         H: int, N: int, d: int, scale: float, causal: int, seed: int, drop_t: int,
+                         stream: int = 0) -> int:
+    """Call the dropout forward's C entry point with raw addresses; returns the status."""
+    return load_library().attn_fwd_dropout(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, N, d,
+                                           ctypes.c_float(scale), causal, seed, drop_t, stream)
+
+
+def attn_fwd_dropout(q, k, v, seed: int, drop_t: int, scale: float | None = None,
+                     causal: bool = False, out=None, lse=None, stream=None):
+    """Fused attention forward with dropout on the probabilities.
+
+    Like ``attn_fwd``; each probability P[i, j] of head b*H + h is kept when
+    its Philox-4x32-10 byte (key ``seed``) is >= ``drop_t`` (drop probability
+    drop_t / 256, 0..255) and the output is scaled by 256 / (256 - drop_t).
+    ``lse`` is the undropped log-normaliser.  Returns (o, lse).
+    """
+    import torch
+    B, H, N, d, out, lse = _fwd_buffers(q, k, v, out, lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = load_library().attn_fwd_dropout(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+        ctypes.c_float(float(scale)), int(bool(causal)), int(seed) & ((1 << 64) - 1), int(drop_t),
+        int(stream))
+    if st != TA_OK:
+        raise RuntimeError("attn_fwd_dropout failed: %s (status %d)" % (attn_status_string(st), st))
     return out, lse
 
 

@@ -88,6 +88,18 @@ __device__ __forceinline__ void sched_mfma_ds(std::integer_sequence<int, I...>) 
    ...);
 }
 
+// Like sched_mfma_ds, with V vector instructions placed after each product.
+template <int PRE, int PER, int TOTAL, int V, int... I>
+__device__ __forceinline__ void sched_mfma_ds_valu(std::integer_sequence<int, I...>) {
+  __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);
+  ((__builtin_amdgcn_sched_group_barrier(0x008, 1, 0),
+    __builtin_amdgcn_sched_group_barrier(
+        0x100, (TOTAL - PRE - PER * I) >= PER ? PER : ((TOTAL - PRE - PER * I) > 0 ? (TOTAL - PRE - PER * I) : 0),
+        0),
+    __builtin_amdgcn_sched_group_barrier(0x002, V, 0)),
+   ...);
+}
+
 // Recipe building blocks: a group of R DS reads, and N repetitions of
 // (1 MFMA, R DS reads, V VALU instructions); empty groups are skipped.
 template <int R>
@@ -273,5 +285,73 @@ struct LdsReaderF8 {
     return __builtin_bit_cast(i32x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
   }
 };
+
+// Philox-4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel random
+// numbers: as easy as 1, 2, 3", SC 2011): counter (c0..c3), key (k0, k1).  Each
+// round multiplies words 0 and 2 by the two round constants into 64-bit
+// products whose halves are mixed with words 1 and 3 and the key; the key
+// advances by two Weyl constants between rounds.
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
+  constexpr uint32_t kM0 = 0xD2511F53u, kM1 = 0xCD9E8D57u;
+  constexpr uint32_t kW0 = 0x9E3779B9u, kW1 = 0xBB67AE85u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += kW0;
+      k1 += kW1;
+    }
+    const uint64_t p0 = (uint64_t)kM0 * c0, p1 = (uint64_t)kM1 * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+  }
+  return u32x4{c0, c1, c2, c3};
+}
+
+// Dropout parameters: key (seed_lo, seed_hi); an element is kept when its
+// random byte is >= t (drop probability t / 256); kept values are scaled by
+// keep_scale = 256 / (256 - t).  The byte of (query row i, key j) of head n is
+// byte j mod 16 (little endian) of the block for counter (i, j / 16, n, 0).
+struct DropoutArgs {
+  uint32_t seed_lo, seed_hi, t;
+  float keep_scale;
+};
+
+// Mask words of one 64-key tile for a lane that holds query row `row` and,
+// in 32-key block kb of a score accumulator, keys 32 kb + 8 g + 4 hi + e
+// (g, e = 0..3): word mw[kb][g] carries those four keys' bytes, e in byte e.
+// The two lanes of a row (one per wave half) need disjoint halves of the
+// tile's four 16-key blocks: each generates the two blocks of 32-key block
+// `hi` and one half-wave swap per word pair trades what the other needs.
+__device__ __forceinline__ void dropout_row_words(uint32_t row, uint32_t tile, uint32_t head,
+                                                  const DropoutArgs& dr, int hi,
+                                                  uint32_t (&mw)[2][4]) {
+  const uint32_t blk = 4u * tile + 2u * (uint32_t)hi;
+  const u32x4 b0 = philox4x32_10(row, blk, head, 0u, dr.seed_lo, dr.seed_hi);
+  const u32x4 b1 = philox4x32_10(row, blk + 1u, head, 0u, dr.seed_lo, dr.seed_hi);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    // Word 2 (g % 2) of block g / 2 serves the lower half (keys 8 g + 0..3),
+    // word 2 (g % 2) + 1 the upper half (keys 8 g + 4..7).  After the swap
+    // the first result holds block kb = 0's word for this lane, the second
+    // block kb = 1's.
+    const uint32_t lo = (g >> 1) ? b1[2 * (g & 1)] : b0[2 * (g & 1)];
+    const uint32_t up = (g >> 1) ? b1[2 * (g & 1) + 1] : b0[2 * (g & 1) + 1];
+    const auto pr = __builtin_amdgcn_permlane32_swap(lo, up, false, false);
+    mw[0][g] = pr[0];
+    mw[1][g] = pr[1];
+  }
+}
+
+// Keep test of element (kb, i) of a score accumulator pair (key
+// 32 kb + 8 (i / 4) + 4 hi + i % 4) with the words of dropout_row_words.
+__device__ __forceinline__ bool dropout_keep(const uint32_t (&mw)[2][4], int kb, int i,
+                                             uint32_t t) {
+  return ((mw[kb][i >> 2] >> (8 * (i & 3))) & 0xffu) >= t;
+}
 
 }  // namespace tiledattn

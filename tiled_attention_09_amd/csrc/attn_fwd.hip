@@ -30,10 +30,10 @@ int launch(const void* q, const void* k, const void* v, float* o, float* lse, in
   // multiply-add per exponent); zero or negative scales take the scaled path.
   if (scale_log2 > 0.f)
     tiledattn::attn_fwd_kernel<D, DV, CAUSAL, true, GENERAL><<<grid, block, 0, stream>>>(
-        qq, kk, vv, o, lse, bh, Nq, Nk, offset, n_qt, scale_log2, nullptr, nullptr);
+        qq, kk, vv, o, lse, bh, Nq, Nk, offset, n_qt, scale_log2, nullptr, nullptr, tiledattn::DropoutArgs{});
   else
     tiledattn::attn_fwd_kernel<D, DV, CAUSAL, false, GENERAL><<<grid, block, 0, stream>>>(
-        qq, kk, vv, o, lse, bh, Nq, Nk, offset, n_qt, scale_log2, nullptr, nullptr);
+        qq, kk, vv, o, lse, bh, Nq, Nk, offset, n_qt, scale_log2, nullptr, nullptr, tiledattn::DropoutArgs{});
   return hipGetLastError() == hipSuccess ? TA_OK : TA_ERR_HIP;
 }
 

@@ -54,6 +54,8 @@ namespace tiledattn {
 
 // Vector instructions of the softmax placed after each score product.
 constexpr int kValuPerMfma = 7;
+// Vector instructions of the dropout generator placed after each value product.
+constexpr int kDropValuPerMfma = 16;
 
 // D: width of Q and K rows; DV: width of V and O rows.  Nq query rows at
 // absolute positions offset .. offset + Nq - 1 attend Nk keys at positions
@@ -62,15 +64,19 @@ constexpr int kValuPerMfma = 7;
 // known at compile time.  F8: Q and K are FP8 (OCP E4M3) codes with per-head
 // descale factors (Q = codes * q_descale[b h], likewise K), the scores use the
 // FP8 matrix product, and the descales fold into the exponent scale (d = 128,
-// square shapes).
-template <int D, int DV, bool CAUSAL, bool POS_SCALE, bool GENERAL, bool F8 = false>
+// square shapes).  DROPOUT: each probability is kept or zeroed by the
+// reproducible mask of `drop` (DropoutArgs) and the output scaled by
+// keep_scale; the normaliser and LSE count every visible key (square shapes).
+template <int D, int DV, bool CAUSAL, bool POS_SCALE, bool GENERAL, bool F8 = false,
+          bool DROPOUT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
                      const uint16_t* __restrict__ V, float* __restrict__ O,
                      float* __restrict__ LSE, int bh_count, int Nq, int nk_arg, int offset_arg,
                      int n_qt, float scale_log2, const float* __restrict__ q_descale,
-                     const float* __restrict__ k_descale) {
+                     const float* __restrict__ k_descale, DropoutArgs drop) {
   static_assert(!F8 || (D == 128 && DV == 128 && !GENERAL), "FP8 scores: d = 128, square");
+  static_assert(!DROPOUT || (!GENERAL && !F8), "dropout: square bf16 shapes");
   const int Nk = GENERAL ? nk_arg : Nq;
   const int offset = GENERAL ? offset_arg : 0;
   using T = Tile<D>;
@@ -207,6 +213,8 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
   // Online-softmax update from a tile's prepared scores s:
   // m' = max(m, max S), alpha = exp(m - m'), p = exp(S - m'), l' = alpha l + sum p.
   // Returns alpha; p goes to pf as the bf16 B operand of the value product.
+  // Dropout mask words of the tile whose softmax runs next (dropout_row_words).
+  uint32_t mw[2][4];
   auto softmax = [&](f32x16 (&s)[2], bf16x8 (&pf)[4]) __attribute__((always_inline)) {
     // Row maximum: 32 in-lane values (a chain of 3-input maxima), then the
     // other wave half.
@@ -232,14 +240,19 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
         const float arg = POS_SCALE ? __builtin_fmaf(s[kb][i], scale_log2, -cref) : s[kb][i] - cref;
         const float p = __builtin_amdgcn_exp2f(arg);
         psum += p;
-        pf[kb * 2 + (i >> 3)][i & 7] = (__bf16)p;
+        // Dropout zeroes the weight in the value product only: the
+        // normaliser keeps every visible key.
+        const float pv = (DROPOUT && !dropout_keep(mw, kb, i, drop.t)) ? 0.f : p;
+        pf[kb * 2 + (i >> 3)][i & 7] = (__bf16)pv;
       }
     l = __builtin_fmaf(l, alpha, psum);
     return alpha;
   };
 
   // O^T (dv x 32 queries) += V^T (dv x 64 keys) P^T (64 keys x 32 queries).
-  auto values = [&](const TA_LDS uint16_t* vt, const bf16x8 (&pf)[4])
+  // With dropout, the mask words of tile j + 1 are generated meanwhile (the
+  // vector unit is otherwise idle during these products).
+  auto values = [&](int j, const TA_LDS uint16_t* vt, const bf16x8 (&pf)[4])
                     __attribute__((always_inline)) {
 #pragma unroll
     for (int g = 0; g < 4; ++g)
@@ -247,8 +260,14 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
       for (int db = 0; db < TV::DB; ++db)
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rdv.col_op(vt, g, db), pf[g], oacc[db],
                                                            0, 0, 0);
-    // Eight transposed V reads in flight, then two more per product.
-    sched_mfma_ds<8, 2, 8 * TV::DB>(std::make_integer_sequence<int, 4 * TV::DB>{});
+    if constexpr (DROPOUT) {
+      dropout_row_words((uint32_t)my_q, (uint32_t)(j + 1), (uint32_t)bh, drop, hi, mw);
+      sched_mfma_ds_valu<8, 2, 8 * TV::DB, kDropValuPerMfma>(
+          std::make_integer_sequence<int, 4 * TV::DB>{});
+    } else {
+      // Eight transposed V reads in flight, then two more per product.
+      sched_mfma_ds<8, 2, 8 * TV::DB>(std::make_integer_sequence<int, 4 * TV::DB>{});
+    }
   };
 
   // Pipeline (the matrix work of the next tile runs under the softmax of this
@@ -291,7 +310,7 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
     }
-    values(v_cur, pf);
+    values(j, v_cur, pf);
   };
   // Iteration j with the stage parity P = j % 2 fixed at compile time.
   auto iter = [&](int j, auto pc) __attribute__((always_inline)) {
@@ -316,6 +335,7 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (n_w > 0) scores(k0, sa);
+    if constexpr (DROPOUT) dropout_row_words((uint32_t)my_q, 0u, (uint32_t)bh, drop, hi, mw);
   }
   for (int j = 0; j < n_kt; j += 2) {
     iter(j, std::integral_constant<int, 0>{});
@@ -329,7 +349,7 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
   const float l_row = l + other_half(l);
   if (my_q < Nq) {
     const bool live = l_row > 0.f;
-    const float inv = live ? 1.f / l_row : 0.f;
+    const float inv = live ? (DROPOUT ? drop.keep_scale : 1.f) / l_row : 0.f;
     float* orow = O + ((size_t)bh * Nq + my_q) * DV;
 #pragma unroll
     for (int db = 0; db < TV::DB; ++db)
