@@ -217,6 +217,25 @@ int attn_bwd(const void* q, const void* k, const void* v, const float* o,
              void* workspace, int B, int H, int N, int d, float scale, int causal,
              void* stream);
 
+/*
+ * attn_bwd_dropout -- the gradients of attn_fwd_dropout (same seed, drop_t,
+ * scale and causal flag).  With M the keep mask (regenerated from the seed,
+ * never stored) and ks = 256 / (256 - drop_t):
+ *
+ *     dV = (P * M ks)^T G,   dP = (G V^T) * M ks,   dS = P * (dP - D),
+ *     D_i = sum_c G[i,c] O[i,c]   (O: attn_fwd_dropout's output)
+ *     dQ = scale dS K,   dK = scale dS^T Q
+ *
+ * (the chain rule of attn_bwd through the mask; the row sum of dP * P still
+ * equals D).  Arguments, workspace (attn_bwd_workspace_size), ownership,
+ * determinism and errors as for attn_bwd; drop_t outside 0 .. 255 gives
+ * TA_ERR_INVALID_ARG.
+ */
+int attn_bwd_dropout(const void* q, const void* k, const void* v, const float* o,
+                     const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                     void* workspace, int B, int H, int N, int d, float scale, int causal,
+                     uint64_t seed, int drop_t, void* stream);
+
 /* Human-readable text for a ta_status value (static storage; never NULL). */
 const char* attn_status_string(int status);
 

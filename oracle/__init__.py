@@ -10,7 +10,8 @@ shares no code with the HIP path.
 * ``e4m3_decode`` / ``e4m3_encode`` / ``quantize_per_head`` -- OCP E4M3 codes
   and the per-head FP8 quantiser of the FP8-score forward.
 * ``philox4x32`` / ``dropout_keep`` / ``attention_dropout_ref`` /
-  ``attention_dropout_bwd_ref`` -- the reproducible dropout mask and attention
+  ``attention_dropout_bwd_ref`` / ``attention_dropout_bwd_ref_rows`` -- the
+  reproducible dropout mask and attention
   forward and backward with it.
 * ``attention_bwd_ref`` / ``attention_bwd_ref_batched`` -- float64 gradients
   dQ, dK, dV by their definition; ``attention_bwd_tiled_ref`` -- the
@@ -30,7 +31,8 @@ tiled method under many tilings.
 from .attention_ref import attention_ref, attention_ref_batched, bf16_bits_to_f64, f32_scale
 from .attention_bwd_ref import (attention_bwd_ref, attention_bwd_ref_batched,
                                 attention_bwd_tiled_ref)
-from .dropout_ref import (attention_dropout_bwd_ref, attention_dropout_ref, dropout_keep,
+from .dropout_ref import (attention_dropout_bwd_ref, attention_dropout_bwd_ref_rows,
+                          attention_dropout_ref, dropout_keep,
                           philox4x32)
 from .fp8_ref import E4M3_MAX, e4m3_decode, e4m3_encode, quantize_per_head
 from .online_ref import all_compositions, online_attention_ref, uniform_bounds
@@ -39,4 +41,5 @@ __all__ = ["attention_ref", "attention_ref_batched", "bf16_bits_to_f64", "f32_sc
            "online_attention_ref", "all_compositions", "uniform_bounds",
            "attention_bwd_ref", "attention_bwd_ref_batched", "attention_bwd_tiled_ref",
            "E4M3_MAX", "e4m3_decode", "e4m3_encode", "quantize_per_head",
-           "philox4x32", "dropout_keep", "attention_dropout_ref", "attention_dropout_bwd_ref"]
+           "philox4x32", "dropout_keep", "attention_dropout_ref", "attention_dropout_bwd_ref",
+           "attention_dropout_bwd_ref_rows"]

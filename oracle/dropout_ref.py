@@ -33,7 +33,8 @@ import numpy as np
 
 from .attention_ref import _visible
 
-__all__ = ["philox4x32", "dropout_keep", "attention_dropout_ref", "attention_dropout_bwd_ref"]
+__all__ = ["philox4x32", "dropout_keep", "attention_dropout_ref", "attention_dropout_bwd_ref",
+           "attention_dropout_bwd_ref_rows"]
 
 _M0 = 0xD2511F53
 _M1 = 0xCD9E8D57
@@ -120,3 +121,30 @@ def attention_dropout_bwd_ref(q, k, v, do, scale: float, causal: bool, n_head: i
     dp = (do @ v.T) * mk
     ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))
     return float(scale) * (ds @ k), float(scale) * (ds.T @ q), dv
+
+
+def attention_dropout_bwd_ref_rows(q, k, v, do, scale: float, causal: bool, n_head: int,
+                                   seed: int, t: int, query_rows=None, key_rows=None,
+                                   chunk: int = 1024):
+    """One head: attention_dropout_bwd_ref's dQ[query_rows], dK[key_rows] and
+    dV[key_rows] (None: all rows), the same formulas evaluated for a chunk of
+    query rows at a time so long sequences fit in memory."""
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    n = q.shape[0]
+    qr = np.arange(n) if query_rows is None else np.asarray(query_rows, dtype=np.int64)
+    kr = np.arange(k.shape[0]) if key_rows is None else np.asarray(key_rows, dtype=np.int64)
+    dq = np.zeros((qr.size, q.shape[1]))
+    dk = np.zeros((kr.size, k.shape[1]))
+    dv = np.zeros((kr.size, v.shape[1]))
+    for c0 in range(0, n, chunk):
+        rows = np.arange(c0, min(n, c0 + chunk))
+        p, _ = _probs(q, k, scale, causal, rows)
+        mk = dropout_keep(n_head, rows, k.shape[0], seed, t) / (1.0 - t / 256.0)
+        dp = (do[rows] @ v.T) * mk
+        ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))
+        dv += (p * mk)[:, kr].T @ do[rows]
+        dk += float(scale) * (ds[:, kr].T @ q[rows])
+        sel = (qr >= c0) & (qr <= rows[-1])
+        if sel.any():
+            dq[sel] = float(scale) * (ds[qr[sel] - c0] @ k)
+    return dq, dk, dv

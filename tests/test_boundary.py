@@ -40,7 +40,8 @@ def declared_functions():
 
 
 def test_header_declares_entry_points():
-    assert declared_functions() == ["attn_bwd", "attn_bwd_workspace_size", "attn_fwd",
+    assert declared_functions() == ["attn_bwd", "attn_bwd_dropout", "attn_bwd_workspace_size",
+                                    "attn_fwd",
                                     "attn_fwd_dropout", "attn_fwd_ex", "attn_fwd_fp8",
                                     "attn_quantize_fp8", "attn_status_string"]
 
@@ -297,3 +298,33 @@ def test_dropout_fwd_head_dims():
 @pytest.mark.parametrize("field,off", [("q", 8), ("v", 4), ("o", 8), ("lse", 2)])
 def test_dropout_fwd_misaligned(field, off):
     assert call_drop(**{field: A + off}) == ta.TA_ERR_MISALIGNED
+
+
+BWD_PTRS = ["q", "k", "v", "o", "lse", "do", "dq", "dk", "dv", "ws"]
+
+
+def call_bwd_drop(**over):
+    args = dict({p: A for p in BWD_PTRS}, B=1, H=2, N=256, d=128, scale=0.09, causal=1,
+                seed=7, t=26)
+    args.update(over)
+    return ta.attn_bwd_dropout_raw(*(args[p] for p in BWD_PTRS), args["B"], args["H"], args["N"],
+                                   args["d"], args["scale"], args["causal"], args["seed"],
+                                   args["t"], 0)
+
+
+@host_only
+@pytest.mark.parametrize("over", [dict(do=0), dict(ws=0), dict(N=0), dict(H=0), dict(causal=-1),
+                                  dict(scale=math.inf), dict(t=-1), dict(t=300)])
+def test_dropout_bwd_invalid(over):
+    assert call_bwd_drop(**over) == ta.TA_ERR_INVALID_ARG
+
+
+@host_only
+def test_dropout_bwd_head_dims():
+    assert call_bwd_drop(d=32) == ta.TA_ERR_UNSUPPORTED
+
+
+@host_only
+@pytest.mark.parametrize("field,off", [("do", 8), ("dk", 4), ("ws", 8), ("lse", 2)])
+def test_dropout_bwd_misaligned(field, off):
+    assert call_bwd_drop(**{field: A + off}) == ta.TA_ERR_MISALIGNED

@@ -1,5 +1,6 @@
-"""GPU parity of attention with dropout (attn_fwd_dropout) against the float64
-oracle, which draws the same Philox-4x32-10 mask on the CPU.
+"""GPU parity of attention with dropout (attn_fwd_dropout, attn_bwd_dropout)
+against the float64 oracle, which draws the same Philox-4x32-10 mask on the
+CPU.
 
 Bars.  drop_t = 0 keeps every probability: the output must equal attn_fwd's
 bit for bit.  Otherwise O = keep_scale * (a masked form of the plain sum) with
@@ -9,6 +10,12 @@ that of the plain forward:
     max |dLSE| <= 1e-3            (LSE counts every visible key: unchanged).
 A wrong mask byte moves an output by the full weight of one key times
 keep_scale, far above these bars.
+
+The backward runs the full path (HIP forward with dropout, then the HIP
+backward) and keeps the plain backward's bars, relative to each exact
+gradient's magnitude (which already carries keep_scale):
+    max |X - X_ref| <= 2^-6 max |X_ref| + 1e-5,
+    mean |X - X_ref| <= 2^-8 mean |X_ref| + 1e-6     for X in dQ, dK, dV.
 """
 from __future__ import annotations
 
@@ -16,13 +23,16 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention_dropout_ref, bf16_bits_to_f64, f32_scale
-from tiled_attention_09_amd.synth import WORKLOADS, bf16_bits, make_qkv, make_workload, sample_rows
+from oracle import (attention_dropout_bwd_ref_rows, attention_dropout_ref, bf16_bits_to_f64,
+                    f32_scale)
+from tiled_attention_09_amd.synth import (WORKLOADS, bf16_bits, make_dout, make_qkv, make_workload,
+                                          sample_rows)
 
 pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
 O_MAX, O_MEAN, LSE_MAX = 1e-2, 1e-3, 1e-3
+MAX_REL, MEAN_REL = 2.0 ** -6, 2.0 ** -8
 
 
 def _ta():
@@ -111,3 +121,84 @@ def test_dropout_forward_headline_sampled():
     q, k, v = make_workload(w)
     rows = [sample_rows(w.N, 32, w.seed + 700 + i) for i in range(w.B * w.H)]
     _check_fwd(q, k, v, w.scale, w.causal, seed=2024, t=26, rows=rows)
+
+
+# ---- backward ------------------------------------------------------------------
+
+def _gpu_bwd(q, k, v, g, scale, causal, seed, t):
+    ta = _ta()
+    qd, kd, vd, gd = (x.to(DEV) for x in (q, k, v, g))
+    o, lse = ta.attn_fwd_dropout(qd, kd, vd, seed, t, scale=scale, causal=causal)
+    grads = ta.attn_bwd_dropout(qd, kd, vd, o, lse, gd, seed, t, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    return tuple(x.cpu().double().numpy() for x in grads)
+
+
+def _check_bwd(got, ref, what):
+    msgs, ok = [], True
+    for name, a, b in zip(("dQ", "dK", "dV"), got, ref):
+        err = np.abs(a - b)
+        mx, mean = np.abs(b).max(), np.abs(b).mean()
+        msgs.append("%s max %.2e (rel %.2e) mean rel %.2e" % (
+            name, err.max(), err.max() / max(mx, 1e-30), err.mean() / max(mean, 1e-30)))
+        ok &= bool(np.all(np.isfinite(a)))
+        ok &= bool(err.max() <= MAX_REL * mx + 1e-5 and err.mean() <= MEAN_REL * mean + 1e-6)
+    msg = "%s: %s" % (what, "; ".join(msgs))
+    print("  " + msg, flush=True)
+    assert ok, msg
+
+
+def _bwd_case(B, H, N, d, causal, t, seed, heads=None, qr=None, kr=None, w=None):
+    scale = 1.0 / np.sqrt(d) if w is None else w.scale
+    if w is None:
+        q, k, v = make_qkv(B, H, N, d, seed)
+        g = make_dout(B, H, N, d, seed)
+    else:
+        q, k, v = make_workload(w)
+        g = make_dout(w.B, w.H, w.N, w.d, w.seed)
+    got = _gpu_bwd(q, k, v, g, scale, causal, seed, t)
+    heads = range(B * H) if heads is None else heads
+    gq, gk, gv, rq, rk, rv = [], [], [], [], [], []
+    for n in heads:
+        b, h = divmod(n, H)
+        ref = attention_dropout_bwd_ref_rows(_f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h]),
+                                             _f64(g[b, h]), f32_scale(scale), causal, n, seed, t,
+                                             qr, kr)
+        sq = slice(None) if qr is None else qr
+        sk = slice(None) if kr is None else kr
+        gq.append(got[0][b, h][sq]); gk.append(got[1][b, h][sk]); gv.append(got[2][b, h][sk])
+        rq.append(ref[0]); rk.append(ref[1]); rv.append(ref[2])
+    return tuple(map(np.stack, (gq, gk, gv))), tuple(map(np.stack, (rq, rk, rv)))
+
+
+@pytest.mark.parametrize("t", [0, 26, 230])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,d", [(1, 64), (65, 128), (333, 64), (1003, 128)])
+def test_dropout_backward_full_rows(N, d, causal, t):
+    print("case dropout bwd N=%d d=%d causal=%d t=%d" % (N, d, causal, t), flush=True)
+    got, ref = _bwd_case(2, 2, N, d, causal, t, seed=3000 + N + d + t)
+    _check_bwd(got, ref, "N=%d d=%d causal=%d t=%d" % (N, d, causal, t))
+
+
+def test_dropout_backward_headline_sampled():
+    """B=2, H=32, N=8192, d=128 causal, Q,K x4, drop probability 26/256: 64
+    sampled query rows (dQ) and key rows (dK, dV) of three heads, full path."""
+    w = WORKLOADS["headline"]
+    print("case dropout bwd headline %s" % w.describe(), flush=True)
+    got, ref = _bwd_case(w.B, w.H, w.N, w.d, w.causal, 26, seed=2025, heads=[0, 37, 63],
+                         qr=sample_rows(w.N, 64, w.seed + 800),
+                         kr=sample_rows(w.N, 64, w.seed + 900), w=w)
+    _check_bwd(got, ref, "headline sampled")
+
+
+def test_dropout_backward_deterministic():
+    ta = _ta()
+    B, H, N, d = 1, 3, 300, 128
+    q, k, v = (x.to(DEV) for x in make_qkv(B, H, N, d, 31))
+    g = make_dout(B, H, N, d, 31).to(DEV)
+    o, lse = ta.attn_fwd_dropout(q, k, v, 9, 64, causal=True)
+    a = ta.attn_bwd_dropout(q, k, v, o, lse, g, 9, 64, causal=True)
+    b = ta.attn_bwd_dropout(q, k, v, o, lse, g, 9, 64, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.isfinite(x).all() and torch.equal(x, y)

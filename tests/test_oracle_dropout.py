@@ -11,8 +11,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (attention_bwd_ref, attention_dropout_bwd_ref, attention_dropout_ref,
-                    attention_ref, dropout_keep, philox4x32)
+from oracle import (attention_bwd_ref, attention_dropout_bwd_ref, attention_dropout_bwd_ref_rows,
+                    attention_dropout_ref, attention_ref, dropout_keep, philox4x32)
 
 _KAT = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "philox4x32_10_kat.json")))
 
@@ -138,3 +138,17 @@ def test_correction_identity_holds_under_dropout():
     mk = dropout_keep(0, np.arange(20), 20, 3, t) / (1 - t / 256)
     dp = (g @ v.T) * mk
     np.testing.assert_allclose((dp * p).sum(axis=1), (g * o).sum(axis=1), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_chunked_rows_equal_the_definition(causal):
+    """attention_dropout_bwd_ref_rows (chunks of query rows, sampled outputs)
+    against attention_dropout_bwd_ref on the same inputs."""
+    rng = np.random.default_rng(13)
+    n, d = 50, 6
+    q, k, v, g = (rng.standard_normal((n, d)) for _ in range(4))
+    full = attention_dropout_bwd_ref(q, k, v, g, 0.3, causal, 6, 17, 70)
+    qr, kr = np.array([0, 7, 16, 49]), np.array([1, 15, 33, 48])
+    part = attention_dropout_bwd_ref_rows(q, k, v, g, 0.3, causal, 6, 17, 70, qr, kr, chunk=16)
+    for a, b in zip(part, (full[0][qr], full[1][kr], full[2][kr])):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)

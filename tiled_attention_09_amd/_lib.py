@@ -51,6 +51,9 @@ def load_library() -> ctypes.CDLL:
         lib.attn_fwd_dropout.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p]
         lib.attn_fwd_dropout.restype = ctypes.c_int
+        lib.attn_bwd_dropout.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 4 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p]
+        lib.attn_bwd_dropout.restype = ctypes.c_int
         lib.attn_status_string.argtypes = [ctypes.c_int]
         lib.attn_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -222,18 +225,9 @@ def attn_bwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, d
                                    stream)
 
 
-def attn_bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False,
-             workspace=None, grads=None, stream=None):
-    """Gradients of ``attn_fwd`` on the GPU.
-
-    q, k, v, do: bfloat16 [B, H, N, d]; o float32 [B, H, N, d] and lse float32
-    [B, H, N] from ``attn_fwd`` with the same scale and causal flag.  Returns
-    (dq, dk, dv), float32 [B, H, N, d].  ``workspace`` (a uint8 device tensor of
-    at least ``attn_bwd_workspace_size`` bytes) and ``grads`` (three float32
-    tensors) may be given to reuse buffers.
-    """
+def _bwd_buffers(q, k, v, o, lse, do, workspace, grads):
+    """Checks of the backward's inputs; returns (B, H, N, d, workspace, grads)."""
     import torch
-    lib = load_library()
     for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16),
                         ("v", v, torch.bfloat16), ("do", do, torch.bfloat16),
                         ("o", o, torch.float32)):
@@ -247,8 +241,6 @@ def attn_bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = Fal
     if not lse.is_cuda or lse.dtype != torch.float32 or lse.shape != (B, H, N) \
             or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 device tensor [B, H, N]")
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
     ws_bytes = attn_bwd_workspace_size(B, H, N)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
@@ -260,6 +252,24 @@ def attn_bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = Fal
     for t in grads:
         if t.shape != (B, H, N, d) or t.dtype != torch.float32 or not t.is_contiguous():
             raise ValueError("grads must be contiguous float32 [B, H, N, d]")
+    return B, H, N, d, workspace, grads
+
+
+def attn_bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False,
+             workspace=None, grads=None, stream=None):
+    """Gradients of ``attn_fwd`` on the GPU.
+
+    q, k, v, do: bfloat16 [B, H, N, d]; o float32 [B, H, N, d] and lse float32
+    [B, H, N] from ``attn_fwd`` with the same scale and causal flag.  Returns
+    (dq, dk, dv), float32 [B, H, N, d].  ``workspace`` (a uint8 device tensor of
+    at least ``attn_bwd_workspace_size`` bytes) and ``grads`` (three float32
+    tensors) may be given to reuse buffers.
+    """
+    import torch
+    lib = load_library()
+    B, H, N, d, workspace, grads = _bwd_buffers(q, k, v, o, lse, do, workspace, grads)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     dq, dk, dv = grads
@@ -269,6 +279,38 @@ def attn_bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = Fal
                       int(bool(causal)), int(stream))
     if st != TA_OK:
         raise RuntimeError("attn_bwd failed: %s (status %d)" % (attn_status_string(st), st))
+    return dq, dk, dv
+
+
+def attn_bwd_dropout_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int,
+                         do_ptr: int, dq_ptr: int, dk_ptr: int, dv_ptr: int, ws_ptr: int, B: int,
+                         H: int, N: int, d: int, scale: float, causal: int, seed: int,
+                         drop_t: int, stream: int = 0) -> int:
+    """Call the dropout backward's C entry point with raw addresses; returns the status."""
+    return load_library().attn_bwd_dropout(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr,
+                                           dk_ptr, dv_ptr, ws_ptr, B, H, N, d,
+                                           ctypes.c_float(scale), causal, seed, drop_t, stream)
+
+
+def attn_bwd_dropout(q, k, v, o, lse, do, seed: int, drop_t: int, scale: float | None = None,
+                     causal: bool = False, workspace=None, grads=None, stream=None):
+    """Gradients of ``attn_fwd_dropout`` (same seed, drop_t, scale, causal): the
+    mask is regenerated, never stored.  Arguments and results as ``attn_bwd``."""
+    import torch
+    lib = load_library()
+    B, H, N, d, workspace, grads = _bwd_buffers(q, k, v, o, lse, do, workspace, grads)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    dq, dk, dv = grads
+    st = lib.attn_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                              dv.data_ptr(), workspace.data_ptr(), B, H, N, d,
+                              ctypes.c_float(float(scale)), int(bool(causal)),
+                              int(seed) & ((1 << 64) - 1), int(drop_t), int(stream))
+    if st != TA_OK:
+        raise RuntimeError("attn_bwd_dropout failed: %s (status %d)" % (attn_status_string(st), st))
     return dq, dk, dv
 
 

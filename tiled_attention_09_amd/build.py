@@ -15,8 +15,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRCS = [os.path.join(HERE, "csrc", f) for f in ("attn_fwd.hip", "attn_bwd.hip", "attn_fp8.hip",
-                                                        "attn_dropout.hip")]
+SRCS = [os.path.join(HERE, "csrc", f) for f in ("attn_fwd.hip", "attn_bwd.hip", "attn_fp8.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libtiledattn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")

@@ -99,15 +99,69 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const float* __restr
   }
 }
 
+// Dropout mask words for a lane that owns key column k_first + (lane % 32) of
+// 32 keys and, in query block qb of a 32 x 32 accumulator pair, tile rows
+// 32 qb + 8 g + 4 hi + e (g, e = 0..3): word out[qb][g] carries rows e = 0..3
+// in byte e (the byte layout dropout_keep reads).
+// Lane L generates the two 16-key blocks (keys k_first .. k_first + 31) of
+// tile row qbase + L; a 4 x 4 byte transpose inside each quad of lanes (rows
+// 4a .. 4a+3) turns four rows x four keys around, and a 2 KB per-wave LDS block
+// (64 bytes per key) hands every lane its column.  In a key's 64 bytes, row
+// group a = 8 qb + 2 g + hi sits at word (hi, qb, g), so a reader's eight words
+// are two aligned 16-byte chunks; chunk c of key k is stored at chunk
+// c ^ ((k / 4) % 4), which keeps the 16-byte reads and the 4-byte writes free
+// of bank conflicts.
+__device__ __forceinline__ void dropout_col_words(uint32_t qbase, uint32_t k_first, uint32_t head,
+                                                  const DropoutArgs& dr, int lane,
+                                                  TA_LDS uint32_t* buf, uint32_t (&out)[2][4]) {
+  const uint32_t blk = k_first >> 4;
+  const u32x4 b0 = philox4x32_10(qbase + (uint32_t)lane, blk, head, 0u, dr.seed_lo, dr.seed_hi);
+  const u32x4 b1 = philox4x32_10(qbase + (uint32_t)lane, blk + 1u, head, 0u, dr.seed_lo,
+                                 dr.seed_hi);
+  // Quad transpose, two exchanges (byte selectors of v_perm_b32: 0-3 pick the
+  // second operand's bytes, 4-7 the first's):
+  //  1. with lane ^ 1: even lanes keep (own 0, partner 0, own 2, partner 2),
+  //     odd lanes (partner 1, own 1, partner 3, own 3);
+  //  2. with lane ^ 2: lanes 0, 1 keep (own 0, own 1, partner 0, partner 1),
+  //     lanes 2, 3 (partner 2, partner 3, own 2, own 3).
+  // Lane 4a + i then holds key 4w + i of rows 4a .. 4a+3 (row 4a + e in byte e).
+  const uint32_t sel1 = (lane & 1) ? 0x03070105u : 0x06020400u;
+  const uint32_t sel2 = (lane & 2) ? 0x03020706u : 0x05040100u;
+  const int a = lane >> 2, i = lane & 3;
+  const int pos = ((a & 1) << 3) | ((a >> 3) << 2) | ((a >> 1) & 3);
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const uint32_t x = (w < 4) ? b0[w] : b1[w - 4];   // keys 4w .. 4w+3 of row qbase + lane
+    const uint32_t px = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);
+    const uint32_t y1 = __builtin_amdgcn_perm(px, x, sel1);
+    const uint32_t py = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)y1, 0x4E, 0xF, 0xF, false);
+    const uint32_t y2 = __builtin_amdgcn_perm(py, y1, sel2);
+    const int key = 4 * w + i;
+    buf[key * 16 + ((((pos >> 2) ^ (key >> 2)) & 3) << 2) + (pos & 3)] = y2;
+  }
+  __builtin_amdgcn_wave_barrier();
+  const int kk = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int c = (2 * hi + qb) ^ ((kk >> 2) & 3);
+    const u32x4 r = *reinterpret_cast<const TA_LDS u32x4*>(buf + kk * 16 + 4 * c);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) out[qb][g] = r[g];
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
 // ---------------------------------------------------------------------------
 // 2. dK and dV for 128 keys of one head per workgroup.
-template <int D, bool CAUSAL>
+// DROPOUT: the probabilities of the forward were kept or zeroed by the mask of
+// `drop` and scaled by keep_scale:  dV = (P M ks)^T G,  dS = P (M ks dP - D).
+template <int D, bool CAUSAL, bool DROPOUT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ G,
                           const f32x2* __restrict__ stats, float* __restrict__ dK,
                           float* __restrict__ dV, int bh_count, int N, int stats_stride,
-                          int n_kt, float c, float scale, int skip_floor) {
+                          int n_kt, float c, float scale, int skip_floor, DropoutArgs drop) {
   using T = Tile<D>;
   __shared__ __attribute__((aligned(1024))) uint16_t q_lds0[kBN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t g_lds0[kBN * D];
@@ -115,6 +169,7 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   __shared__ __attribute__((aligned(1024))) uint16_t g_lds1[kBN * D];
   __shared__ __attribute__((aligned(16))) float st_lds0[2 * kBN];   // {LSE2, D} per query row
   __shared__ __attribute__((aligned(16))) float st_lds1[2 * kBN];
+  __shared__ __attribute__((aligned(16))) uint32_t mk_lds[DROPOUT ? kWaves * 32 * 16 : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -170,6 +225,11 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     // products below yield dP - D directly.
     f32x16 s[2], dp[2];
     float lse2[2][16];
+    float dd[DROPOUT ? 2 : 1][16];   // dropout: D itself, the dP accumulator starts at 0
+    uint32_t mk[2][4];
+    if constexpr (DROPOUT)
+      dropout_col_words((uint32_t)qbase, (uint32_t)k0, (uint32_t)bh, drop, lane,
+                        (TA_LDS uint32_t*)mk_lds + wave * (32 * 16), mk);
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int qb = r >> 2, g4 = r & 3;
@@ -180,10 +240,19 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
       lse2[qb][4 * g4 + 1] = a[2];
       lse2[qb][4 * g4 + 2] = b[0];
       lse2[qb][4 * g4 + 3] = b[2];
-      dp[qb][4 * g4 + 0] = -a[1];
-      dp[qb][4 * g4 + 1] = -a[3];
-      dp[qb][4 * g4 + 2] = -b[1];
-      dp[qb][4 * g4 + 3] = -b[3];
+      if constexpr (DROPOUT) {
+        dd[qb][4 * g4 + 0] = a[1];
+        dd[qb][4 * g4 + 1] = a[3];
+        dd[qb][4 * g4 + 2] = b[1];
+        dd[qb][4 * g4 + 3] = b[3];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) dp[qb][4 * g4 + t] = 0.f;
+      } else {
+        dp[qb][4 * g4 + 0] = -a[1];
+        dp[qb][4 * g4 + 1] = -a[3];
+        dp[qb][4 * g4 + 2] = -b[1];
+        dp[qb][4 * g4 + 3] = -b[3];
+      }
     }
     // S and dP - D: 2 blocks of 32 queries x the wave's 32 keys (4 KS products).
 #pragma unroll
@@ -229,8 +298,17 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float p = __builtin_amdgcn_exp2f(s[qb][e]);
-        pf[2 * qb + (e >> 3)][e & 7] = (__bf16)p;
-        sf[2 * qb + (e >> 3)][e & 7] = (__bf16)(p * dp[qb][e]);
+        if constexpr (DROPOUT) {
+          // dV uses P M (keep_scale is applied to dV once, at the end).
+          const bool keep = dropout_keep(mk, qb, e, drop.t);
+          pf[2 * qb + (e >> 3)][e & 7] = (__bf16)(keep ? p : 0.f);
+          const float g = keep ? __builtin_fmaf(drop.keep_scale, dp[qb][e], -dd[qb][e])
+                               : -dd[qb][e];
+          sf[2 * qb + (e >> 3)][e & 7] = (__bf16)(p * g);
+        } else {
+          pf[2 * qb + (e >> 3)][e & 7] = (__bf16)p;
+          sf[2 * qb + (e >> 3)][e & 7] = (__bf16)(p * dp[qb][e]);
+        }
       }
 
     // dV^T (d x 32 keys) += G^T (d x 64 queries) P;  dK^T += Q^T dS.
@@ -298,7 +376,9 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
       for (int g = 0; g < 4; ++g) {
         f32x4 a = {dk[db][4 * g] * scale, dk[db][4 * g + 1] * scale, dk[db][4 * g + 2] * scale,
                    dk[db][4 * g + 3] * scale};
-        f32x4 b = {dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]};
+        const float vs = DROPOUT ? drop.keep_scale : 1.f;
+        f32x4 b = {dv[db][4 * g] * vs, dv[db][4 * g + 1] * vs, dv[db][4 * g + 2] * vs,
+                   dv[db][4 * g + 3] * vs};
         *reinterpret_cast<f32x4*>(dkrow + db * 32 + 8 * g + 4 * hi) = a;
         *reinterpret_cast<f32x4*>(dvrow + db * 32 + 8 * g + 4 * hi) = b;
       }
@@ -307,13 +387,14 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 
 // ---------------------------------------------------------------------------
 // 3. dQ for 128 query rows of one head per workgroup.
-template <int D, bool CAUSAL>
+// DROPOUT: dS = P (M ks dP - D) with the forward's mask (dropout_row_words).
+template <int D, bool CAUSAL, bool DROPOUT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                         const uint16_t* __restrict__ V, const uint16_t* __restrict__ G,
                         const f32x2* __restrict__ stats, float* __restrict__ dQ, int bh_count,
                         int N, int stats_stride, int n_qt, float c, float scale,
-                        int skip_ceiling) {
+                        int skip_ceiling, DropoutArgs drop) {
   using T = Tile<D>;
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[kBN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[kBN * D];
@@ -370,6 +451,8 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   auto compute_tile = [&](int j, const TA_LDS uint16_t* kt, const TA_LDS uint16_t* vt) {
     const int key0 = j * kBN;
     const bool edge = (CAUSAL && key0 + kBN - 1 > q0) || (key0 + kBN > N);
+    uint32_t mw[2][4];
+    if constexpr (DROPOUT) dropout_row_words((uint32_t)my_q, (uint32_t)j, (uint32_t)bh, drop, hi, mw);
     // One 32-key block at a time: S^T and dP^T (32 keys x 32 queries), then
     // its dS^T, then its share of dQ^T.
 #pragma unroll
@@ -405,8 +488,12 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
       }
       bf16x8 sf[2];
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        sf[e >> 3][e & 7] = (__bf16)(__builtin_amdgcn_exp2f(s[e]) * (dp[e] - dd));
+      for (int e = 0; e < 16; ++e) {
+        float g = dp[e] - dd;
+        if constexpr (DROPOUT)
+          g = dropout_keep(mw, kb, e, drop.t) ? __builtin_fmaf(drop.keep_scale, dp[e], -dd) : -dd;
+        sf[e >> 3][e & 7] = (__bf16)(__builtin_amdgcn_exp2f(s[e]) * g);
+      }
 
       // dQ^T (d x 32 queries) += K^T (d x these 32 keys) dS^T.
 #pragma unroll
