@@ -1,7 +1,8 @@
 """Benchmark: fused attention forward TFLOP/s on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline]
-                    [--no-cpu-baseline] [--no-backward]
+                    [--no-cpu-baseline] [--no-backward] [--no-fp8] [--no-dropout]
+                    [--no-general]
 
 A step is one attention forward over the whole workload (B=2, H=32, N=8192,
 d=128, causal, Q and K scaled by 4 -- the headline case) with inputs already
@@ -16,7 +17,9 @@ a bounded sample of the same workload on the host cores.  ``backward`` reports
 the gradient pass (attn_bwd: row statistics, dK/dV and dQ kernels) on the same
 workload and output gradient, timed the same way after the forward's timing;
 its flops are the algorithmic 2.5x of the forward's (five N^2 d products
-instead of two).
+instead of two).  ``fp8_scores``, ``dropout`` and ``general_shapes`` time the
+FP8-score forward, the forward and backward with dropout, and the
+general-shape forward the same way.
 """
 from __future__ import annotations
 
@@ -228,6 +231,63 @@ def time_fp8(w, q, k, v, stream, steps: int, warmup: int):
             "steps": steps, "warmup": warmup}
 
 
+def _timed(fn, stream, steps: int, warmup: int) -> float:
+    """Average ms of `fn` over `steps` calls after `warmup` untimed ones, from
+    HIP events recorded on the launch stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+DROP_T = 26            # drop probability 26/256 (about 0.1)
+DROP_SEED = 2024
+
+
+def time_dropout(w, q, k, v, stream, steps: int, warmup: int):
+    """Time attn_fwd_dropout and attn_bwd_dropout (drop probability
+    DROP_T/256) on the workload; the flop counts are those of the plain
+    forward and backward (the mask adds no products)."""
+    import torch
+
+    import tiled_attention_09_amd as ta
+    from tiled_attention_09_amd.synth import make_dout
+    dev = q.device
+    sc = stream.cuda_stream
+    o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    g = make_dout(w.B, w.H, w.N, w.d, w.seed).to(dev)
+    ws = torch.empty(ta.attn_bwd_workspace_size(w.B, w.H, w.N), dtype=torch.uint8, device=dev)
+    grads = tuple(torch.empty_like(o) for _ in range(3))
+
+    def fwd():
+        ta.attn_fwd_dropout(q, k, v, DROP_SEED, DROP_T, w.scale, w.causal, out=o, lse=lse,
+                            stream=sc)
+
+    def bwd():
+        ta.attn_bwd_dropout(q, k, v, o, lse, g, DROP_SEED, DROP_T, w.scale, w.causal,
+                            workspace=ws, grads=grads, stream=sc)
+
+    out = {"metric": "attention TFLOP/s with dropout (Philox-4x32-10 masks regenerated in "
+                     "the kernels)", "drop_t": DROP_T, "drop_probability": DROP_T / 256.0,
+           "steps": steps, "warmup": warmup}
+    for name, fn, flops in (("forward", fwd, w.flops), ("backward", bwd, w.bwd_flops)):
+        ms = _timed(fn, stream, steps, warmup)
+        tf = flops / (ms * 1e-3) / 1e12
+        out[name] = {"kernel_ms": round(ms, 5), "tflops": round(tf, 2),
+                     "roofline": {"bound": "mfma", "achieved": round(tf, 2),
+                                  "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
+    return out
+
+
 # General-shape forward workloads (attn_fwd_ex): name, B, H, Nq, Nk, d, dv, offset, causal.
 GENERAL = [
     ("chunked prefill: 1024 queries at positions 7168.. of 8192 keys", 2, 32, 1024, 8192, 128, 128,
@@ -298,6 +358,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-general", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-dropout", action="store_true")
     ap.add_argument("--counter-pass", action="store_true",
                     help="run the calibration copy and a few launches for rocprofv3 --pmc")
     args = ap.parse_args()
@@ -394,6 +455,8 @@ def main():
         out["backward"] = time_backward(w, q, k, v, o, lse, stream, args.steps, args.warmup)
     if not args.no_fp8:
         out["fp8_scores"] = time_fp8(w, q, k, v, stream, args.steps, args.warmup)
+    if not args.no_dropout:
+        out["dropout"] = time_dropout(w, q, k, v, stream, args.steps, args.warmup)
     if not args.no_general:
         del q, k, v, o, lse
         torch.cuda.empty_cache()
