@@ -13,7 +13,8 @@ shares no code with the HIP path.
   ``attention_dropout_bwd_ref`` / ``attention_dropout_bwd_ref_rows`` -- the
   reproducible dropout mask and attention
   forward and backward with it.
-* ``attention_bwd_ref`` / ``attention_bwd_ref_batched`` -- float64 gradients
+* ``attention_bwd_ref`` / ``attention_bwd_ref_batched`` /
+  ``attention_bwd_dq_rows_ref`` / ``attention_bwd_kv_rows_ref`` -- float64 gradients
   dQ, dK, dV by their definition; ``attention_bwd_tiled_ref`` -- the
   recomputing tiled backward, pinned against the definition.
 
@@ -29,7 +30,8 @@ scale), invariants (key shift, value shift, query/key scale symmetry), and the
 tiled method under many tilings.
 """
 from .attention_ref import attention_ref, attention_ref_batched, bf16_bits_to_f64, f32_scale
-from .attention_bwd_ref import (attention_bwd_ref, attention_bwd_ref_batched,
+from .attention_bwd_ref import (attention_bwd_dq_rows_ref, attention_bwd_kv_rows_ref,
+                                attention_bwd_ref, attention_bwd_ref_batched,
                                 attention_bwd_tiled_ref)
 from .dropout_ref import (attention_dropout_bwd_ref, attention_dropout_bwd_ref_rows,
                           attention_dropout_ref, dropout_keep,
@@ -40,6 +42,7 @@ from .online_ref import all_compositions, online_attention_ref, uniform_bounds
 __all__ = ["attention_ref", "attention_ref_batched", "bf16_bits_to_f64", "f32_scale",
            "online_attention_ref", "all_compositions", "uniform_bounds",
            "attention_bwd_ref", "attention_bwd_ref_batched", "attention_bwd_tiled_ref",
+           "attention_bwd_dq_rows_ref", "attention_bwd_kv_rows_ref",
            "E4M3_MAX", "e4m3_decode", "e4m3_encode", "quantize_per_head",
            "philox4x32", "dropout_keep", "attention_dropout_ref", "attention_dropout_bwd_ref",
            "attention_dropout_bwd_ref_rows"]

@@ -40,7 +40,8 @@ import numpy as np
 
 from .attention_ref import _visible, attention_ref
 
-__all__ = ["attention_bwd_ref", "attention_bwd_tiled_ref", "attention_bwd_ref_batched"]
+__all__ = ["attention_bwd_ref", "attention_bwd_tiled_ref", "attention_bwd_ref_batched",
+           "attention_bwd_dq_rows_ref", "attention_bwd_kv_rows_ref"]
 
 
 def _as64(*xs):
@@ -145,3 +146,35 @@ def attention_bwd_ref_batched(q, k, v, do, scale: float, causal: bool = False,
             if sel.any():
                 dq[n, sel] = float(scale) * (ds[qr[sel] - c0] @ kh)
     return dq, dk, dvo
+
+
+def attention_bwd_dq_rows_ref(q, k, v, do, scale: float, causal: bool = False, rows=None,
+                              query_offset: int = 0):
+    """dQ[rows] of attention_bwd_ref for one head.  Row i of dQ depends only on
+    row i of P, dP and dS, so the definition restricted to the chosen rows
+    needs no other query: P_i by the two-pass softmax, dP_i = G_i V^T,
+    dS_i = P_i * (dP_i - sum_j dP_ij P_ij), dQ_i = scale dS_i K."""
+    q, k, v, do = _as64(q, k, v, do)
+    _check(q, k, v, do)
+    rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    p = _softmax_rows(q, k, scale, causal, query_offset, rows)
+    dp = do[rows] @ v.T
+    ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))
+    return float(scale) * (ds @ k)
+
+
+def attention_bwd_kv_rows_ref(q, k, v, do, scale: float, causal: bool, key_rows, query_rows,
+                              query_offset: int = 0):
+    """dK[key_rows], dV[key_rows] of attention_bwd_ref for one head, summing the
+    key columns of dS and P over `query_rows` only:
+        dV_j = sum_i P_ij G_i,   dK_j = scale sum_i dS_ij q_i   (i in query_rows).
+    Exact when query_rows holds every query that sees the keys (under the
+    causal mask with offset 0, keys j >= j0 are seen only by queries i >= j0)."""
+    q, k, v, do = _as64(q, k, v, do)
+    _check(q, k, v, do)
+    kr = np.asarray(key_rows, dtype=np.int64)
+    qr = np.asarray(query_rows, dtype=np.int64)
+    p = _softmax_rows(q, k, scale, causal, query_offset, qr)
+    dp = do[qr] @ v.T
+    ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))
+    return float(scale) * (ds[:, kr].T @ q[qr]), p[:, kr].T @ do[qr]

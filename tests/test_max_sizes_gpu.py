@@ -1,0 +1,126 @@
+"""GPU parity at the largest sequence the entry points accept (N = 2^22 keys
+per head, the limit attn_fwd / attn_fwd_ex / attn_bwd check), in one head.
+
+Every compared value has an exact oracle that does not need the whole
+N x N problem:
+  * forward: sampled query rows (tile edges, the middle, the last rows);
+  * decoding: one query at position N - 1 over all N keys (attn_fwd_ex);
+  * backward: dQ of sampled rows (row i of dQ needs only row i of P), and dK,
+    dV of the last 64 keys, which under the causal mask only the last 64
+    queries see; plus the identities sum_j dK_j = 0 and sum_j dV_j = sum_i G_i
+    that hold at any size.
+Bars as in the other parity tests (forward: max |dO| <= 1e-2, mean <= 1e-3,
+max |dLSE| <= 1e-3; backward: max <= 2^-6 max |ref| + 1e-5, mean <= 2^-8
+mean |ref| + 1e-6 per gradient).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import (attention_bwd_dq_rows_ref, attention_bwd_kv_rows_ref, attention_ref,
+                    bf16_bits_to_f64, f32_scale)
+from tiled_attention_09_amd.synth import bf16_bits, make_dout, make_qkv
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+N_MAX = 1 << 22
+O_MAX, O_MEAN, LSE_MAX = 1e-2, 1e-3, 1e-3
+MAX_REL, MEAN_REL = 2.0 ** -6, 2.0 ** -8
+
+
+def _ta():
+    import tiled_attention_09_amd as ta
+    ta.load_library()
+    return ta
+
+
+def _f64(t):
+    return bf16_bits_to_f64(bf16_bits(t))
+
+
+def _rows(n, seed):
+    fixed = [0, 1, 63, 64, 127, 128, 129, n // 2, n - 129, n - 128, n - 65, n - 64, n - 2, n - 1]
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([fixed, rng.integers(0, n, 6)])).astype(np.int64)
+
+
+def _check_fwd(o, lse, ro, rl, what):
+    do, dl = np.abs(o - ro), np.abs(lse - rl)
+    msg = "%s: max|dO| %.3e mean|dO| %.3e max|dLSE| %.3e" % (what, do.max(), do.mean(), dl.max())
+    print("  " + msg, flush=True)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), msg
+    assert do.max() <= O_MAX and do.mean() <= O_MEAN and dl.max() <= LSE_MAX, msg
+
+
+def _check_grad(name, got, ref):
+    err = np.abs(got - ref)
+    mx, mean = np.abs(ref).max(), np.abs(ref).mean()
+    msg = "%s max %.2e (rel %.2e) mean rel %.2e" % (name, err.max(), err.max() / mx,
+                                                    err.mean() / mean)
+    print("  " + msg, flush=True)
+    assert np.all(np.isfinite(got)), msg
+    assert err.max() <= MAX_REL * mx + 1e-5 and err.mean() <= MEAN_REL * mean + 1e-6, msg
+
+
+def test_forward_longest_sequence():
+    print("case max-size forward B=1 H=1 N=2^22 d=128 causal", flush=True)
+    q, k, v = make_qkv(1, 1, N_MAX, 128, 2201)
+    scale = 1.0 / np.sqrt(128)
+    o, lse = _ta().attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), scale=scale, causal=True)
+    torch.cuda.synchronize()
+    rows = _rows(N_MAX, 2202)
+    o = o[0, 0].cpu().double().numpy()[rows]
+    lse = lse[0, 0].cpu().double().numpy()[rows]
+    ro, rl = attention_ref(_f64(q[0, 0]), _f64(k[0, 0]), _f64(v[0, 0]), f32_scale(scale), True,
+                           rows=rows)
+    _check_fwd(o, lse, ro, rl, "N=2^22 rows %d" % rows.size)
+
+
+def test_decode_over_longest_key_sequence():
+    print("case max-size decode Nq=1 Nk=2^22 offset 2^22-1", flush=True)
+    g = torch.Generator().manual_seed(2203)
+    q = torch.randn((1, 2, 1, 128), generator=g).to(torch.bfloat16)
+    k = torch.randn((1, 2, N_MAX, 128), generator=g).to(torch.bfloat16)
+    v = torch.randn((1, 2, N_MAX, 128), generator=g).to(torch.bfloat16)
+    scale = 1.0 / np.sqrt(128)
+    o, lse = _ta().attn_fwd_ex(q.to(DEV), k.to(DEV), v.to(DEV), scale=scale, causal=True,
+                               query_offset=N_MAX - 1)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    for h in range(2):
+        ro, rl = attention_ref(_f64(q[0, h]), _f64(k[0, h]), _f64(v[0, h]), f32_scale(scale), True,
+                               query_offset=N_MAX - 1)
+        _check_fwd(o[0, h], lse[0, h], ro, rl, "decode head %d" % h)
+
+
+def test_backward_longest_sequence():
+    print("case max-size backward B=1 H=1 N=2^22 d=128 causal", flush=True)
+    ta = _ta()
+    q, k, v = make_qkv(1, 1, N_MAX, 128, 2204)
+    g = make_dout(1, 1, N_MAX, 128, 2204)
+    scale = 1.0 / np.sqrt(128)
+    qd, kd, vd, gd = (t.to(DEV) for t in (q, k, v, g))
+    o, lse = ta.attn_fwd(qd, kd, vd, scale=scale, causal=True)
+    dq, dk, dv = ta.attn_bwd(qd, kd, vd, o, lse, gd, scale=scale, causal=True)
+    torch.cuda.synchronize()
+    del qd, kd, vd, gd, o, lse
+    dq, dk, dv = (x[0, 0].cpu() for x in (dq, dk, dv))
+    qf, kf, vf, gf = (_f64(t[0, 0]) for t in (q, k, v, g))
+    rows = _rows(N_MAX, 2205)
+    _check_grad("dQ rows", dq.double().numpy()[rows],
+                attention_bwd_dq_rows_ref(qf, kf, vf, gf, f32_scale(scale), True, rows))
+    tail = np.arange(N_MAX - 64, N_MAX)
+    rk, rv = attention_bwd_kv_rows_ref(qf, kf, vf, gf, f32_scale(scale), True, tail, tail)
+    _check_grad("dK last 64 keys", dk.double().numpy()[tail], rk)
+    _check_grad("dV last 64 keys", dv.double().numpy()[tail], rv)
+    # Identities over all keys (exact arithmetic: sum_j dS_ij = 0 and sum_j P_ij = 1).
+    sk = dk.double().sum(dim=0).numpy()
+    sv, sg = dv.double().sum(dim=0).numpy(), torch.from_numpy(gf).sum(dim=0).numpy()
+    ak, av = dk.double().abs().sum(dim=0).numpy(), dv.double().abs().sum(dim=0).numpy()
+    msg = "sum dK %.2e (of sum|dK| %.2e); sum dV - sum G %.2e (of sum|dV| %.2e)" % (
+        np.abs(sk).max(), ak.max(), np.abs(sv - sg).max(), av.max())
+    print("  " + msg, flush=True)
+    assert np.all(np.abs(sk) <= 1e-4 * ak) and np.all(np.abs(sv - sg) <= 1e-4 * av), msg

@@ -10,7 +10,9 @@ import numpy as np
 import pytest
 
 import oracle_bwd_pins as pins
-from oracle import (all_compositions, attention_bwd_ref, attention_bwd_ref_batched,
+from oracle import (all_compositions, attention_bwd_dq_rows_ref, attention_bwd_kv_rows_ref,
+                    attention_bwd_ref,
+                    attention_bwd_ref_batched,
                     attention_bwd_tiled_ref, uniform_bounds)
 
 
@@ -97,6 +99,36 @@ MUTANTS = {
     "dv_from_ds": dict(dv_from="ds"),
     "mask_off_by_one": dict(mask="off_by_one"),
 }
+
+
+@pytest.mark.parametrize("causal,offset,nq,nk", [(False, 0, 40, 40), (True, 0, 40, 40),
+                                                 (True, 25, 15, 40), (False, 0, 9, 30)])
+def test_dq_rows_equal_the_definition(causal, offset, nq, nk):
+    """attention_bwd_dq_rows_ref on chosen rows against attention_bwd_ref's full dQ."""
+    rng = np.random.default_rng(41)
+    q = rng.standard_normal((nq, 6))
+    k = rng.standard_normal((nk, 6))
+    v = rng.standard_normal((nk, 5))
+    g = rng.standard_normal((nq, 5))
+    rows = np.array([0, 3, nq - 1])
+    full = attention_bwd_ref(q, k, v, g, 0.45, causal, offset)[0]
+    got = attention_bwd_dq_rows_ref(q, k, v, g, 0.45, causal, rows, offset)
+    np.testing.assert_allclose(got, full[rows], rtol=0, atol=1e-13)
+
+
+def test_kv_rows_of_causal_tail_equal_the_definition():
+    """Causal: keys j >= j0 are seen only by queries i >= j0, so summing over
+    those queries gives the full dK and dV rows; other query sets do not."""
+    rng = np.random.default_rng(43)
+    n = 60
+    q, k, v, g = (rng.standard_normal((n, 6)) for _ in range(4))
+    dq, dk, dv = attention_bwd_ref(q, k, v, g, 0.5, True)
+    keys = np.arange(48, n)
+    got_k, got_v = attention_bwd_kv_rows_ref(q, k, v, g, 0.5, True, keys, np.arange(48, n))
+    np.testing.assert_allclose(got_k, dk[keys], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(got_v, dv[keys], rtol=0, atol=1e-13)
+    short_k, _ = attention_bwd_kv_rows_ref(q, k, v, g, 0.5, True, keys, np.arange(50, n))
+    assert np.abs(short_k - dk[keys]).max() > 1e-3
 
 
 def test_generic_copy_is_sound():

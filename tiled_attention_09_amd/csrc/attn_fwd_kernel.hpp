@@ -227,7 +227,12 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
     const float m_new = fmaxf(m, mx);
     const float ref = (m_new == -__builtin_inff()) ? 0.f : m_new;
     const float cref = POS_SCALE ? ref * scale_log2 : ref;
-    const float alpha = __builtin_amdgcn_exp2f((POS_SCALE ? m * scale_log2 : m) - cref);
+    // alpha is exactly 1 while the maximum stays put.  (Formed as
+    // exp2(c m - cref), it would be 1 only up to the rounding of cref: the
+    // subtraction contracts into a fused multiply-add, and a factor 1 - 2^-24
+    // applied on every tile of a long row drifts l by 0.6 % over 5e4 tiles.)
+    const float alpha = (m_new == m) ? 1.f
+                                     : __builtin_amdgcn_exp2f((POS_SCALE ? m * scale_log2 : m) - cref);
     m = m_new;
     // p = 2^(c s - c m'); positive scale: one fused multiply-add per element.
     // The row maximum itself gets p = 1 exactly, so the dominant weight carries
