@@ -171,8 +171,9 @@ int attn_fwd_dropout(const void* q, const void* k, const void* v, float* o, floa
 
 /*
  * attn_bwd_workspace_size -- bytes of device workspace attn_bwd needs for
- * (B, H, N): 8 * B * H * (N rounded up to even).  Returns 0 when the sizes are
- * out of the range attn_bwd accepts.
+ * (B, H, N): 8 * B * H * (N rounded up to even); for attn_bwd_ex pass N = Nq.
+ * Returns 0 when the sizes are out of the range the backward accepts (N = 0
+ * gives 0 bytes, valid for attn_bwd_ex only).
  */
 size_t attn_bwd_workspace_size(int B, int H, int N);
 
@@ -216,6 +217,28 @@ int attn_bwd(const void* q, const void* k, const void* v, const float* o,
              const float* lse, const void* dout, float* dq, float* dk, float* dv,
              void* workspace, int B, int H, int N, int d, float scale, int causal,
              void* stream);
+
+/*
+ * attn_bwd_ex -- the gradients of attn_fwd_ex: general shapes, with the same
+ * formulas as attn_bwd.  Query i sits at position query_offset + i and (when
+ * causal) sees key j iff j <= i + query_offset.
+ *
+ *   q, dout   : device bf16, [B, H, Nq, d] and [B, H, Nq, dv].
+ *   k, v      : device bf16, [B, H, Nk, d] and [B, H, Nk, dv].
+ *   o, lse    : device fp32, [B, H, Nq, dv] and [B, H, Nq] -- attn_fwd_ex's
+ *               outputs for the same inputs, scale, causal flag and offset.
+ *   dq        : device fp32 [B, H, Nq, d]; dk: [B, H, Nk, d]; dv: [B, H, Nk, dv];
+ *               written (every element; dK = dV = 0 for Nq = 0, dQ = 0 for
+ *               Nk = 0).
+ *   workspace : attn_bwd_workspace_size(B, H, Nq) bytes (per query row).
+ *   Nq, Nk    : 0 .. 2^22;  query_offset: 0 .. 2^30;  d, dv: 64 or 128.
+ *   A pointer may be NULL only where its tensors are empty.  Other arguments,
+ *   ownership, determinism and errors as for attn_bwd.
+ */
+int attn_bwd_ex(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                const void* dout, float* dq, float* dk, float* dv, void* workspace, int B, int H,
+                int Nq, int Nk, int d, int dv_width, int query_offset, float scale, int causal,
+                void* stream);
 
 /*
  * attn_bwd_dropout -- the gradients of attn_fwd_dropout (same seed, drop_t,

@@ -40,7 +40,8 @@ def declared_functions():
 
 
 def test_header_declares_entry_points():
-    assert declared_functions() == ["attn_bwd", "attn_bwd_dropout", "attn_bwd_workspace_size",
+    assert declared_functions() == ["attn_bwd", "attn_bwd_dropout", "attn_bwd_ex",
+                                    "attn_bwd_workspace_size",
                                     "attn_fwd",
                                     "attn_fwd_dropout", "attn_fwd_ex", "attn_fwd_fp8",
                                     "attn_quantize_fp8", "attn_status_string"]
@@ -328,3 +329,44 @@ def test_dropout_bwd_head_dims():
 @pytest.mark.parametrize("field,off", [("do", 8), ("dk", 4), ("ws", 8), ("lse", 2)])
 def test_dropout_bwd_misaligned(field, off):
     assert call_bwd_drop(**{field: A + off}) == ta.TA_ERR_MISALIGNED
+
+
+def call_bwd_ex(**over):
+    args = dict({p: A for p in BWD_PTRS}, B=1, H=2, Nq=100, Nk=300, d=128, dvw=64, off=200,
+                scale=0.09, causal=1)
+    args.update(over)
+    return ta.attn_bwd_ex_raw(*(args[p] for p in BWD_PTRS), args["B"], args["H"], args["Nq"],
+                              args["Nk"], args["d"], args["dvw"], args["off"], args["scale"],
+                              args["causal"], 0)
+
+
+@host_only
+@pytest.mark.parametrize("over", [dict(Nq=-1), dict(Nk=(1 << 22) + 1), dict(off=-1),
+                                  dict(off=(1 << 30) + 1), dict(causal=3), dict(scale=math.nan),
+                                  dict(B=0), dict(q=0), dict(k=0), dict(ws=0), dict(dk=0)])
+def test_bwd_ex_invalid(over):
+    assert call_bwd_ex(**over) == ta.TA_ERR_INVALID_ARG
+
+
+@host_only
+@pytest.mark.parametrize("over", [dict(d=32), dict(dvw=96)])
+def test_bwd_ex_head_dims(over):
+    assert call_bwd_ex(**over) == ta.TA_ERR_UNSUPPORTED
+
+
+@host_only
+@pytest.mark.parametrize("field,off", [("q", 8), ("v", 4), ("dv", 8), ("lse", 2), ("ws", 4)])
+def test_bwd_ex_misaligned(field, off):
+    assert call_bwd_ex(**{field: A + off}) == ta.TA_ERR_MISALIGNED
+
+
+@host_only
+def test_bwd_ex_empty_is_a_no_op():
+    assert call_bwd_ex(Nq=0, Nk=0, **{p: 0 for p in BWD_PTRS}) == ta.TA_OK
+
+
+@host_only
+def test_bwd_square_entry_still_rejects_empty():
+    lib = ta.load_library()
+    assert ta.attn_bwd_raw(*([A] * 10), 1, 2, 0, 128, 0.1, 1, 0) == ta.TA_ERR_INVALID_ARG
+    assert lib.attn_bwd_workspace_size(1, 2, 0) == 0

@@ -51,6 +51,9 @@ def load_library() -> ctypes.CDLL:
         lib.attn_fwd_dropout.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p]
         lib.attn_fwd_dropout.restype = ctypes.c_int
+        lib.attn_bwd_ex.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 7 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+        lib.attn_bwd_ex.restype = ctypes.c_int
         lib.attn_bwd_dropout.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 4 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p]
         lib.attn_bwd_dropout.restype = ctypes.c_int
@@ -279,6 +282,65 @@ def attn_bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = Fal
                       int(bool(causal)), int(stream))
     if st != TA_OK:
         raise RuntimeError("attn_bwd failed: %s (status %d)" % (attn_status_string(st), st))
+    return dq, dk, dv
+
+
+def attn_bwd_ex_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, do_ptr: int,
+                    dq_ptr: int, dk_ptr: int, dv_ptr: int, ws_ptr: int, B: int, H: int, Nq: int,
+                    Nk: int, d: int, dv: int, query_offset: int, scale: float, causal: int,
+                    stream: int = 0) -> int:
+    """Call the general-shape backward's C entry point with raw addresses; returns the status."""
+    return load_library().attn_bwd_ex(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr,
+                                      dv_ptr, ws_ptr, B, H, Nq, Nk, d, dv, query_offset,
+                                      ctypes.c_float(scale), causal, stream)
+
+
+def attn_bwd_ex(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False,
+                query_offset: int = 0, workspace=None, grads=None, stream=None):
+    """Gradients of ``attn_fwd_ex`` on the GPU (same scale, causal flag, offset).
+
+    q, do: bf16 [B, H, Nq, d] and [B, H, Nq, dv]; k, v: bf16 [B, H, Nk, d],
+    [B, H, Nk, dv]; o float32 [B, H, Nq, dv], lse float32 [B, H, Nq].  Returns
+    (dq [B, H, Nq, d], dk [B, H, Nk, d], dv [B, H, Nk, dv]), float32.
+    """
+    import torch
+    lib = load_library()
+    for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16),
+                        ("v", v, torch.bfloat16), ("do", do, torch.bfloat16),
+                        ("o", o, torch.float32), ("lse", lse, torch.float32)):
+        if not t.is_cuda or t.dtype != dt or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous %s device tensor" % (name, dt))
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, rows, width]")
+    B, H, Nq, d = (int(x) for x in q.shape)
+    Nk, dvw = int(k.shape[2]), int(v.shape[3])
+    if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape[:3]) != (B, H, Nk):
+        raise ValueError("k must be [B, H, Nk, d] and v [B, H, Nk, dv]")
+    if tuple(do.shape) != (B, H, Nq, dvw) or tuple(o.shape) != (B, H, Nq, dvw) \
+            or tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("do and o must be [B, H, Nq, dv], lse [B, H, Nq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    ws_bytes = attn_bwd_workspace_size(B, H, Nq)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    if workspace.numel() * workspace.element_size() < ws_bytes or not workspace.is_cuda:
+        raise ValueError("workspace must be a device buffer of at least %d bytes" % ws_bytes)
+    shapes = ((B, H, Nq, d), (B, H, Nk, d), (B, H, Nk, dvw))
+    if grads is None:
+        grads = tuple(torch.empty(sh, dtype=torch.float32, device=q.device) for sh in shapes)
+    for t, sh in zip(grads, shapes):
+        if tuple(t.shape) != sh or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("grads must be contiguous float32 dq %s, dk %s, dv %s" % shapes)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    dq, dk, dv = grads
+    st = lib.attn_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                         do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                         workspace.data_ptr(), B, H, Nq, Nk, d, dvw, int(query_offset),
+                         ctypes.c_float(float(scale)), int(bool(causal)), int(stream))
+    if st != TA_OK:
+        raise RuntimeError("attn_bwd_ex failed: %s (status %d)" % (attn_status_string(st), st))
     return dq, dk, dv
 
 

@@ -153,20 +153,30 @@ __device__ __forceinline__ void dropout_col_words(uint32_t qbase, uint32_t k_fir
 
 // ---------------------------------------------------------------------------
 // 2. dK and dV for 128 keys of one head per workgroup.
+// D: width of Q and K rows (dK); DV: width of V, O and G rows (dV).  Nq query
+// rows at positions offset .. offset + Nq - 1 and Nk keys (causal: key j is
+// visible to query i iff j <= i + offset); GENERAL = false is the square case
+// (Nk = Nq, offset 0) with those facts known at compile time.
 // DROPOUT: the probabilities of the forward were kept or zeroed by the mask of
 // `drop` and scaled by keep_scale:  dV = (P M ks)^T G,  dS = P (M ks dP - D).
-template <int D, bool CAUSAL, bool DROPOUT = false>
+template <int D, int DV, bool CAUSAL, bool GENERAL, bool DROPOUT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ G,
                           const f32x2* __restrict__ stats, float* __restrict__ dK,
-                          float* __restrict__ dV, int bh_count, int N, int stats_stride,
-                          int n_kt, float c, float scale, int skip_floor, DropoutArgs drop) {
-  using T = Tile<D>;
+                          float* __restrict__ dV, int bh_count, int Nq, int nk_arg,
+                          int offset_arg, int stats_stride, int n_kt, float c, float scale,
+                          int skip_floor, DropoutArgs drop) {
+  static_assert(GENERAL || D == DV, "square instances have one head width");
+  static_assert(!DROPOUT || !GENERAL, "dropout: square shapes");
+  const int Nk = GENERAL ? nk_arg : Nq;
+  const int offset = GENERAL ? offset_arg : 0;
+  using T = Tile<D>;     // Q and K rows, dK
+  using TG = Tile<DV>;   // G and V rows, dV
   __shared__ __attribute__((aligned(1024))) uint16_t q_lds0[kBN * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t g_lds0[kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t g_lds0[kBN * DV];
   __shared__ __attribute__((aligned(1024))) uint16_t q_lds1[kBN * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t g_lds1[kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t g_lds1[kBN * DV];
   __shared__ __attribute__((aligned(16))) float st_lds0[2 * kBN];   // {LSE2, D} per query row
   __shared__ __attribute__((aligned(16))) float st_lds1[2 * kBN];
   __shared__ __attribute__((aligned(16))) uint32_t mk_lds[DROPOUT ? kWaves * 32 * 16 : 4];
@@ -180,41 +190,46 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   int bh, kt;
   map_block(blockIdx.x, bh_count, n_kt, false, bh, kt);   // causal: key tile 0 (most work) first
 
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2u;
-  const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t gr = make_rsrc(G + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t sr = make_rsrc(stats + (size_t)bh * stats_stride, (uint32_t)N * 8u);
+  const size_t qhead = (size_t)bh * (size_t)Nq, khead = (size_t)bh * (size_t)Nk;
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + qhead * D, (uint32_t)Nq * D * 2u);
+  const __amdgpu_buffer_rsrc_t gr = make_rsrc(G + qhead * DV, (uint32_t)Nq * DV * 2u);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + khead * D, (uint32_t)Nk * D * 2u);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + khead * DV, (uint32_t)Nk * DV * 2u);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(stats + (size_t)bh * stats_stride, (uint32_t)Nq * 8u);
 
   const int k0 = kt * kBM + wave * 32;    // first key of this wave
   const int my_k = k0 + l32;              // this lane's key
 
   // K and V rows of the wave's keys (B operands, k = d): [my_k][16 ks + 8 hi + 0..7].
-  bf16x8 kf[T::KS], vf[T::KS];
+  bf16x8 kf[T::KS], vf[TG::KS];
+  constexpr int KSM = T::KS > TG::KS ? T::KS : TG::KS;
 #pragma unroll
-  for (int ks = 0; ks < T::KS; ++ks) {
-    const uint32_t off = (uint32_t)(my_k * D + 16 * ks + 8 * hi) * 2u;
-    kf[ks] = __builtin_bit_cast(bf16x8, load16(kr, off));
-    vf[ks] = __builtin_bit_cast(bf16x8, load16(vr, off));
+  for (int ks = 0; ks < KSM; ++ks) {
+    if (ks < T::KS)
+      kf[ks] = __builtin_bit_cast(bf16x8, load16(kr, (uint32_t)(my_k * D + 16 * ks + 8 * hi) * 2u));
+    if (ks < TG::KS)
+      vf[ks] = __builtin_bit_cast(bf16x8, load16(vr, (uint32_t)(my_k * DV + 16 * ks + 8 * hi) * 2u));
   }
 
-  uint32_t src_off[T::LOADS];
-  tile_src_offsets<D>(src_off, wave, lane);
+  uint32_t src_q[T::LOADS], src_g[TG::LOADS];
+  tile_src_offsets<D>(src_q, wave, lane);
+  tile_src_offsets<DV>(src_g, wave, lane);
   const LdsReader<D> rd(lane);
+  const LdsReader<DV> rdg(lane);
 
-  f32x16 dk[T::DB], dv[T::DB];
+  f32x16 dk[T::DB], dv[TG::DB];
 #pragma unroll
   for (int db = 0; db < T::DB; ++db)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dk[db][i] = 0.f;
-      dv[db][i] = 0.f;
-    }
+    for (int i = 0; i < 16; ++i) dk[db][i] = 0.f;
+#pragma unroll
+  for (int db = 0; db < TG::DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dv[db][i] = 0.f;
 
-  const int n_qt = (N + kBN - 1) / kBN;
-  const int i0 = CAUSAL ? (kt * kBM) / kBN : 0;   // first query tile that sees any key here
+  const int n_qt = (Nq + kBN - 1) / kBN;
+  // First query tile that sees any key here: its last position reaches kt kBM.
+  const int i0 = CAUSAL ? (GENERAL ? max(0, kt * kBM - offset) : kt * kBM) / kBN : 0;
 
   auto compute_tile = [&](int i, const TA_LDS uint16_t* qt, const TA_LDS uint16_t* gt,
                           const TA_LDS float* st) {
@@ -267,17 +282,18 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ks], s[qb], 0, 0, 0);
       }
 #pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks)
+    for (int ks = 0; ks < TG::KS; ++ks)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const bf16x8 ag = rd.row_op(gt, qb, ks);
+        const bf16x8 ag = rdg.row_op(gt, qb, ks);
         dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, vf[ks], dp[qb], 0, 0, 0);
       }
-    sched_mfma_ds<20, 1, 4 * T::KS + 16>(std::make_integer_sequence<int, 4 * T::KS>{});
+    sched_mfma_ds<20, 1, 2 * (T::KS + TG::KS) + 16>(
+        std::make_integer_sequence<int, 2 * (T::KS + TG::KS)>{});
 
     // Exponent arguments c s - LSE2; hidden pairs (query before key, or query
     // past the end) get -inf, which exp2 turns into an exact 0.
-    const bool edge = (CAUSAL && qbase < k0 + 31) || (qbase + kBN > N);
+    const bool edge = (CAUSAL && qbase + offset < k0 + 31) || (qbase + kBN > Nq);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -288,7 +304,7 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int q = qbase + 32 * qb + 8 * (e >> 2) + 4 * hi + (e & 3);
-          if ((CAUSAL && my_k > q) || q >= N) s[qb][e] = -__builtin_inff();
+          if ((CAUSAL && my_k > q + offset) || q >= Nq) s[qb][e] = -__builtin_inff();
         }
     }
     // P = 2^arg and dS = P (dP - D), rounded to bf16 as B operands.
@@ -311,17 +327,22 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         }
       }
 
-    // dV^T (d x 32 keys) += G^T (d x 64 queries) P;  dK^T += Q^T dS.
+    // dV^T (dv x 32 keys) += G^T (dv x 64 queries) P;  dK^T (d x 32) += Q^T dS.
+    constexpr int DBM = T::DB > TG::DB ? T::DB : TG::DB;
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int db = 0; db < T::DB; ++db) {
-        const bf16x8 ag = rd.col_op(gt, g, db);
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, pf[g], dv[db], 0, 0, 0);
-        const bf16x8 aq = rd.col_op(qt, g, db);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sf[g], dk[db], 0, 0, 0);
+      for (int db = 0; db < DBM; ++db) {
+        if (db < TG::DB) {
+          const bf16x8 ag = rdg.col_op(gt, g, db);
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, pf[g], dv[db], 0, 0, 0);
+        }
+        if (db < T::DB) {
+          const bf16x8 aq = rd.col_op(qt, g, db);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, sf[g], dk[db], 0, 0, 0);
+        }
       }
-    sched_mfma_ds<8, 2, 16 * T::DB>(std::make_integer_sequence<int, 8 * T::DB>{});
+    sched_mfma_ds<8, 2, 8 * (T::DB + TG::DB)>(std::make_integer_sequence<int, 4 * (T::DB + TG::DB)>{});
   };
 
   TA_LDS uint16_t* const q0p = (TA_LDS uint16_t*)q_lds0;
@@ -335,26 +356,26 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   // INT_MIN as skip_floor: the test is then always true, but stays a runtime
   // branch, which keeps each tile's products in a scheduling region of its own
   // (merged regions made the compiler spill).
-  const int first_key = CAUSAL ? k0 : skip_floor;
+  const int first_key = CAUSAL ? k0 - offset : skip_floor;
   auto active = [&](int i) { return i * kBN + kBN - 1 >= first_key; };
   // Each stage holds the Q and G rows of one query tile and their {LSE2, D}.
   // Pairs of tiles run in the loop (stage 0, stage 1); an odd last tile runs
   // after it, so the loop has a single exit.
   if (i0 < n_qt) {
-    issue_tile<D>(qr, gr, src_off, i0, wave, q0p, g0p);
+    issue_pair<D, DV>(qr, gr, src_q, src_g, i0, wave, q0p, g0p);
     issue_stats(sr, i0, wave, lane, s0p);
   }
   int i = i0;
   for (; i + 1 < n_qt; i += 2) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();                       // tile i visible; tile i-1's readers done
-    issue_tile<D>(qr, gr, src_off, i + 1, wave, q1p, g1p);
+    issue_pair<D, DV>(qr, gr, src_q, src_g, i + 1, wave, q1p, g1p);
     issue_stats(sr, i + 1, wave, lane, s1p);
     if (active(i)) compute_tile(i, q0p, g0p, s0p);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (i + 2 < n_qt) {
-      issue_tile<D>(qr, gr, src_off, i + 2, wave, q0p, g0p);
+      issue_pair<D, DV>(qr, gr, src_q, src_g, i + 2, wave, q0p, g0p);
       issue_stats(sr, i + 2, wave, lane, s0p);
     }
     if (active(i + 1)) compute_tile(i + 1, q1p, g1p, s1p);
@@ -367,39 +388,50 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 
   // Epilogue: lane owns key my_k; accumulator element e of block db is column
   // 32 db + 8 (e / 4) + 4 hi + e % 4.
-  if (my_k < N) {
-    float* dkrow = dK + head + (size_t)my_k * D;
-    float* dvrow = dV + head + (size_t)my_k * D;
+  if (my_k < Nk) {
+    float* dkrow = dK + (khead + my_k) * D;
+    float* dvrow = dV + (khead + my_k) * DV;
+    constexpr int DBM = T::DB > TG::DB ? T::DB : TG::DB;
 #pragma unroll
-    for (int db = 0; db < T::DB; ++db)
+    for (int db = 0; db < DBM; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        f32x4 a = {dk[db][4 * g] * scale, dk[db][4 * g + 1] * scale, dk[db][4 * g + 2] * scale,
-                   dk[db][4 * g + 3] * scale};
-        const float vs = DROPOUT ? drop.keep_scale : 1.f;
-        f32x4 b = {dv[db][4 * g] * vs, dv[db][4 * g + 1] * vs, dv[db][4 * g + 2] * vs,
-                   dv[db][4 * g + 3] * vs};
-        *reinterpret_cast<f32x4*>(dkrow + db * 32 + 8 * g + 4 * hi) = a;
-        *reinterpret_cast<f32x4*>(dvrow + db * 32 + 8 * g + 4 * hi) = b;
+        if (db < T::DB) {
+          f32x4 a = {dk[db][4 * g] * scale, dk[db][4 * g + 1] * scale, dk[db][4 * g + 2] * scale,
+                     dk[db][4 * g + 3] * scale};
+          *reinterpret_cast<f32x4*>(dkrow + db * 32 + 8 * g + 4 * hi) = a;
+        }
+        if (db < TG::DB) {
+          const float vs = DROPOUT ? drop.keep_scale : 1.f;
+          f32x4 b = {dv[db][4 * g] * vs, dv[db][4 * g + 1] * vs, dv[db][4 * g + 2] * vs,
+                     dv[db][4 * g + 3] * vs};
+          *reinterpret_cast<f32x4*>(dvrow + db * 32 + 8 * g + 4 * hi) = b;
+        }
       }
   }
 }
 
 // ---------------------------------------------------------------------------
 // 3. dQ for 128 query rows of one head per workgroup.
+// Shapes as for the dK/dV kernel (D, DV, Nq, Nk, offset, GENERAL).
 // DROPOUT: dS = P (M ks dP - D) with the forward's mask (dropout_row_words).
-template <int D, bool CAUSAL, bool DROPOUT = false>
+template <int D, int DV, bool CAUSAL, bool GENERAL, bool DROPOUT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                         const uint16_t* __restrict__ V, const uint16_t* __restrict__ G,
                         const f32x2* __restrict__ stats, float* __restrict__ dQ, int bh_count,
-                        int N, int stats_stride, int n_qt, float c, float scale,
-                        int skip_ceiling, DropoutArgs drop) {
-  using T = Tile<D>;
+                        int Nq, int nk_arg, int offset_arg, int stats_stride, int n_qt, float c,
+                        float scale, int skip_ceiling, DropoutArgs drop) {
+  static_assert(GENERAL || D == DV, "square instances have one head width");
+  static_assert(!DROPOUT || !GENERAL, "dropout: square shapes");
+  const int Nk = GENERAL ? nk_arg : Nq;
+  const int offset = GENERAL ? offset_arg : 0;
+  using T = Tile<D>;     // Q and K rows, dQ
+  using TV = Tile<DV>;   // G and V rows
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[kBN * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[kBN * DV];
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[kBN * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[kBN * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[kBN * DV];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -410,34 +442,35 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   int bh, qt;
   map_block(blockIdx.x, bh_count, n_qt, CAUSAL, bh, qt);
 
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2u;
-  const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t gr = make_rsrc(G + head, head_bytes);
+  const size_t qhead = (size_t)bh * (size_t)Nq, khead = (size_t)bh * (size_t)Nk;
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + qhead * D, (uint32_t)Nq * D * 2u);
+  const __amdgpu_buffer_rsrc_t gr = make_rsrc(G + qhead * DV, (uint32_t)Nq * DV * 2u);
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + khead * D, (uint32_t)Nk * D * 2u);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + khead * DV, (uint32_t)Nk * DV * 2u);
 
   const int q0 = qt * kBM + wave * 32;
   const int my_q = q0 + l32;
 
   // Q and G rows of the lane's query (B operands of S^T = K Q^T, dP^T = V G^T).
-  bf16x8 qf[T::KS], gf[T::KS];
+  bf16x8 qf[T::KS], gf[TV::KS];
 #pragma unroll
-  for (int ks = 0; ks < T::KS; ++ks) {
-    const uint32_t off = (uint32_t)(my_q * D + 16 * ks + 8 * hi) * 2u;
-    qf[ks] = __builtin_bit_cast(bf16x8, load16(qr, off));
-    gf[ks] = __builtin_bit_cast(bf16x8, load16(gr, off));
-  }
+  for (int ks = 0; ks < T::KS; ++ks)
+    qf[ks] = __builtin_bit_cast(bf16x8, load16(qr, (uint32_t)(my_q * D + 16 * ks + 8 * hi) * 2u));
+#pragma unroll
+  for (int ks = 0; ks < TV::KS; ++ks)
+    gf[ks] = __builtin_bit_cast(bf16x8, load16(gr, (uint32_t)(my_q * DV + 16 * ks + 8 * hi) * 2u));
   float lse2 = 0.f, dd = 0.f;
-  if (my_q < N) {
+  if (my_q < Nq) {
     const f32x2 st = stats[(size_t)bh * stats_stride + my_q];
     lse2 = st[0];
     dd = st[1];
   }
 
-  uint32_t src_off[T::LOADS];
-  tile_src_offsets<D>(src_off, wave, lane);
+  uint32_t src_k[T::LOADS], src_v[TV::LOADS];
+  tile_src_offsets<D>(src_k, wave, lane);
+  tile_src_offsets<DV>(src_v, wave, lane);
   const LdsReader<D> rd(lane);
+  const LdsReader<DV> rdv(lane);
 
   f32x16 dq[T::DB];
 #pragma unroll
@@ -445,12 +478,13 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 #pragma unroll
     for (int i = 0; i < 16; ++i) dq[db][i] = 0.f;
 
-  const int n_kt_all = (N + kBN - 1) / kBN;
-  const int n_kt = CAUSAL ? min(n_kt_all, (qt + 1) * (kBM / kBN)) : n_kt_all;
+  const int n_kt_all = (Nk + kBN - 1) / kBN;
+  // Causal: key tiles up to the last row's position.
+  const int n_kt = CAUSAL ? min(n_kt_all, (qt * kBM + kBM + offset + kBN - 1) / kBN) : n_kt_all;
 
   auto compute_tile = [&](int j, const TA_LDS uint16_t* kt, const TA_LDS uint16_t* vt) {
     const int key0 = j * kBN;
-    const bool edge = (CAUSAL && key0 + kBN - 1 > q0) || (key0 + kBN > N);
+    const bool edge = (CAUSAL && key0 + kBN - 1 > q0 + offset) || (key0 + kBN > Nk);
     uint32_t mw[2][4];
     if constexpr (DROPOUT) dropout_row_words((uint32_t)my_q, (uint32_t)j, (uint32_t)bh, drop, hi, mw);
     // One 32-key block at a time: S^T and dP^T (32 keys x 32 queries), then
@@ -469,11 +503,11 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[ks], s, 0, 0, 0);
       }
 #pragma unroll
-      for (int ks = 0; ks < T::KS; ++ks) {
-        const bf16x8 av = rd.row_op(vt, kb, ks);
+      for (int ks = 0; ks < TV::KS; ++ks) {
+        const bf16x8 av = rdv.row_op(vt, kb, ks);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, gf[ks], dp, 0, 0, 0);
       }
-      sched_mfma_ds<4, 1, 2 * T::KS>(std::make_integer_sequence<int, 2 * T::KS>{});
+      sched_mfma_ds<4, 1, T::KS + TV::KS>(std::make_integer_sequence<int, T::KS + TV::KS>{});
 
       // Element e is key key0 + 32 kb + 8 (e / 4) + 4 hi + e % 4 of query my_q;
       // hidden keys get exponent -inf (an exact 0).
@@ -483,7 +517,7 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = key0 + kb * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
-          if ((CAUSAL && key > my_q) || key >= N) s[e] = -__builtin_inff();
+          if ((CAUSAL && key > my_q + offset) || key >= Nk) s[e] = -__builtin_inff();
         }
       }
       bf16x8 sf[2];
@@ -511,28 +545,28 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   // wave's last query.  Without the causal mask the host passes INT_MAX as
   // skip_ceiling: always true, but a runtime branch that keeps the two tiles
   // of an iteration in separate scheduling regions.
-  const int last_query = CAUSAL ? q0 + 31 : skip_ceiling;
+  const int last_query = CAUSAL ? q0 + 31 + offset : skip_ceiling;
   auto active = [&](int j) { return j * kBN <= last_query; };
 
   TA_LDS uint16_t* const k0p = (TA_LDS uint16_t*)k_lds0;
   TA_LDS uint16_t* const v0p = (TA_LDS uint16_t*)v_lds0;
   TA_LDS uint16_t* const k1p = (TA_LDS uint16_t*)k_lds1;
   TA_LDS uint16_t* const v1p = (TA_LDS uint16_t*)v_lds1;
-  issue_tile<D>(kr, vr, src_off, 0, wave, k0p, v0p);
+  if (n_kt > 0) issue_pair<D, DV>(kr, vr, src_k, src_v, 0, wave, k0p, v0p);
   for (int j = 0; j < n_kt; j += 2) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (j + 1 < n_kt) issue_tile<D>(kr, vr, src_off, j + 1, wave, k1p, v1p);
+    if (j + 1 < n_kt) issue_pair<D, DV>(kr, vr, src_k, src_v, j + 1, wave, k1p, v1p);
     if (active(j)) compute_tile(j, k0p, v0p);
     if (j + 1 >= n_kt) break;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (j + 2 < n_kt) issue_tile<D>(kr, vr, src_off, j + 2, wave, k0p, v0p);
+    if (j + 2 < n_kt) issue_pair<D, DV>(kr, vr, src_k, src_v, j + 2, wave, k0p, v0p);
     if (active(j + 1)) compute_tile(j + 1, k1p, v1p);
   }
 
-  if (my_q < N) {
-    float* row = dQ + head + (size_t)my_q * D;
+  if (my_q < Nq) {
+    float* row = dQ + (qhead + my_q) * D;
 #pragma unroll
     for (int db = 0; db < T::DB; ++db)
 #pragma unroll
