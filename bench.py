@@ -299,9 +299,11 @@ GENERAL = [
 
 
 def time_general(stream, steps: int, warmup: int):
-    """Time attn_fwd_ex on the GENERAL workloads (seeded bf16 normal inputs).
-    Flops count the visible (query, key) pairs: 2 (d + dv) per pair; bytes are
-    Q, K, V read once and O, LSE written once."""
+    """Time attn_fwd_ex on the GENERAL workloads (seeded bf16 normal inputs),
+    and attn_bwd_ex on the same shapes except the decoding step.  Flops count
+    the visible (query, key) pairs: 2 (d + dv) per pair forward, 2 (3 d + 2 dv)
+    backward (S recomputed, dP, dV, dK, dQ); forward bytes are Q, K, V read
+    once and O, LSE written once."""
     import torch
 
     import tiled_attention_09_amd as ta
@@ -340,10 +342,33 @@ def time_general(stream, steps: int, warmup: int):
                  "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None} if hbm_bound else
                 {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                  "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None})
-        res.append({"workload": name, "B": B, "H": H, "Nq": Nq, "Nk": Nk, "d": d, "dv": dv,
-                    "query_offset": off, "causal": causal, "kernel_ms": round(ms, 5),
-                    "tflops": round(tflops, 2), "gbs": round(gbs, 1), "flops": flops,
-                    "alg_bytes": nbytes, "roofline": roof, "steps": steps})
+        entry = {"workload": name, "B": B, "H": H, "Nq": Nq, "Nk": Nk, "d": d, "dv": dv,
+                 "query_offset": off, "causal": causal, "kernel_ms": round(ms, 5),
+                 "tflops": round(tflops, 2), "gbs": round(gbs, 1), "flops": flops,
+                 "alg_bytes": nbytes, "roofline": roof, "steps": steps}
+        if Nq > 1:
+            g_out = torch.randn((B, H, Nq, dv), generator=g).to(torch.bfloat16).to(dev)
+            ws = torch.empty(max(ta.attn_bwd_workspace_size(B, H, Nq), 16), dtype=torch.uint8,
+                             device=dev)
+            grads = (torch.empty((B, H, Nq, d), dtype=torch.float32, device=dev),
+                     torch.empty((B, H, Nk, d), dtype=torch.float32, device=dev),
+                     torch.empty((B, H, Nk, dv), dtype=torch.float32, device=dev))
+
+            def bwd():
+                ta.attn_bwd_ex(q, k, v, o, lse, g_out, 1.0 / d ** 0.5, causal, off, workspace=ws,
+                               grads=grads, stream=stream.cuda_stream)
+
+            bms = _timed(bwd, stream, steps, warmup)
+            bflops = 2.0 * (3 * d + 2 * dv) * B * H * pairs
+            btf = bflops / (bms * 1e-3) / 1e12
+            entry["backward"] = {"kernel_ms": round(bms, 5), "tflops": round(btf, 2),
+                                 "flops": bflops,
+                                 "roofline": {"bound": "mfma", "achieved": round(btf, 2),
+                                              "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                              "frac": round(btf / PEAK_BF16_TFLOPS, 4),
+                                              "traffic": None}}
+            del g_out, ws, grads
+        res.append(entry)
         del q, k, v, o, lse
     return res
 
