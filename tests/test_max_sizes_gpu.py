@@ -19,8 +19,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (attention_bwd_dq_rows_ref, attention_bwd_kv_rows_ref, attention_ref,
-                    bf16_bits_to_f64, f32_scale)
+from oracle import (attention_bwd_dq_rows_ref, attention_bwd_kv_rows_ref, attention_dropout_ref,
+                    attention_ref, bf16_bits_to_f64, f32_scale)
 from tiled_attention_09_amd.synth import bf16_bits, make_dout, make_qkv
 
 pytestmark = pytest.mark.gpu
@@ -77,6 +77,27 @@ def test_forward_longest_sequence():
     ro, rl = attention_ref(_f64(q[0, 0]), _f64(k[0, 0]), _f64(v[0, 0]), f32_scale(scale), True,
                            rows=rows)
     _check_fwd(o, lse, ro, rl, "N=2^22 rows %d" % rows.size)
+
+
+def test_dropout_forward_longest_sequence():
+    """Dropout masks at row and key indices up to 2^22 - 1 (Philox counters)."""
+    print("case max-size dropout forward B=1 H=1 N=2^22 d=128 causal drop_t=26", flush=True)
+    q, k, v = make_qkv(1, 1, N_MAX, 128, 2206)
+    scale = 1.0 / np.sqrt(128)
+    seed, t = 0xDEADBEEF12345678, 26
+    o, lse = _ta().attn_fwd_dropout(q.to(DEV), k.to(DEV), v.to(DEV), seed, t, scale=scale,
+                                    causal=True)
+    torch.cuda.synchronize()
+    rows = _rows(N_MAX, 2207)
+    o = o[0, 0].cpu().double().numpy()[rows]
+    lse = lse[0, 0].cpu().double().numpy()[rows]
+    ro, rl = attention_dropout_ref(_f64(q[0, 0]), _f64(k[0, 0]), _f64(v[0, 0]), f32_scale(scale),
+                                   True, 0, seed, t, rows=rows)
+    ks = 256.0 / (256.0 - t)
+    do, dl = np.abs(o - ro), np.abs(lse - rl)
+    msg = "dropout N=2^22: max|dO| %.3e mean|dO| %.3e max|dLSE| %.3e" % (do.max(), do.mean(), dl.max())
+    print("  " + msg, flush=True)
+    assert do.max() <= O_MAX * ks and do.mean() <= O_MEAN * ks and dl.max() <= LSE_MAX, msg
 
 
 def test_decode_over_longest_key_sequence():
