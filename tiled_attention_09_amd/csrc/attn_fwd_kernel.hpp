@@ -156,8 +156,10 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
   const int q_last = q0 + 31 + offset;   // position of the wave's last query row
 
   // Tiles this wave takes part in: key tiles whose first key is not past the
-  // wave's last query position (a prefix of 0 .. n_kt - 1).
-  const int n_w = CAUSAL ? min(n_kt, q_last / kBN + 1) : n_kt;
+  // wave's last query position (a prefix of 0 .. n_kt - 1); none when all of
+  // its rows lie past the last query (a ragged last tile, a decoding step):
+  // such a wave only shares the tile copies and barriers.
+  const int n_w = (q0 >= Nq) ? 0 : (CAUSAL ? min(n_kt, q_last / kBN + 1) : n_kt);
 
   // S^T (64 keys x 32 queries) of the key tile in `kt`: block kb covers tile
   // keys 32 kb + [0, 32).
