@@ -295,12 +295,15 @@ GENERAL = [
     ("value width 64: B=2,H=32,N=8192,d=128,dv=64", 2, 32, 8192, 8192, 128, 64, 0, True),
     ("decode step: 1 query at position 8191 of 8192 keys, B=16,H=32", 16, 32, 1, 8192, 128, 128,
      8191, True),
+    ("decode step, few sequences: 16 queries at positions 32752.. of 32768 keys, B=2,H=8", 2, 8,
+     16, 32768, 128, 128, 32752, True),
 ]
 
 
 def time_general(stream, steps: int, warmup: int):
     """Time attn_fwd_ex on the GENERAL workloads (seeded bf16 normal inputs),
-    and attn_bwd_ex on the same shapes except the decoding step.  Flops count
+    attn_fwd_split where it plans a split of the keys, and attn_bwd_ex on the
+    shapes with more than one query.  Flops count
     the visible (query, key) pairs: 2 (d + dv) per pair forward, 2 (3 d + 2 dv)
     backward (S recomputed, dP, dV, dK, dQ); forward bytes are Q, K, V read
     once and O, LSE written once."""
@@ -368,6 +371,27 @@ def time_general(stream, steps: int, warmup: int):
                                               "frac": round(btf / PEAK_BF16_TFLOPS, 4),
                                               "traffic": None}}
             del g_out, ws, grads
+        ws_bytes = ta.attn_fwd_split_workspace_size(B, H, Nq, Nk, dv)
+        if ws_bytes > 0:
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+            def split():
+                ta.attn_fwd_split(q, k, v, 1.0 / d ** 0.5, causal, off, out=o, lse=lse,
+                                  workspace=ws, stream=stream.cuda_stream)
+
+            sms = _timed(split, stream, steps, warmup)
+            sgbs = nbytes / (sms * 1e-3) / 1e9
+            stf = flops / (sms * 1e-3) / 1e12
+            entry["split_keys"] = {
+                "kernel_ms": round(sms, 5), "tflops": round(stf, 2), "gbs": round(sgbs, 1),
+                "workspace_bytes": ws_bytes,
+                "roofline": ({"bound": "hbm", "achieved": round(sgbs, 1), "peak": PEAK_HBM_GBS,
+                              "unit": "GB/s", "frac": round(sgbs / PEAK_HBM_GBS, 4), "traffic": None}
+                             if hbm_bound else
+                             {"bound": "mfma", "achieved": round(stf, 2), "peak": PEAK_BF16_TFLOPS,
+                              "unit": "TFLOP/s", "frac": round(stf / PEAK_BF16_TFLOPS, 4),
+                              "traffic": None})}
+            del ws
         res.append(entry)
         del q, k, v, o, lse
     return res

@@ -143,6 +143,40 @@ int attn_fwd_fp8(const void* q8, const void* k8, const void* v, float* o, float*
                  float scale, int causal, void* stream);
 
 /*
+ * attn_fwd_split_workspace_size -- bytes of device workspace attn_fwd_split
+ * uses for these sizes (0: no split is planned, and attn_fwd_split is
+ * attn_fwd_ex).  Returns 0 also for sizes out of range.
+ */
+size_t attn_fwd_split_workspace_size(int B, int H, int Nq, int Nk, int dv);
+
+/*
+ * attn_fwd_split -- attn_fwd_ex with the key range split over workgroups when
+ * the (batch, head, 128-query tile) grid alone would leave most of the chip
+ * idle (a decoding step of a few sequences over a long context).  Workgroup
+ * (s, head, tile) runs the online softmax over key tiles [s T, (s + 1) T) and
+ * writes its own normalised O_s and LSE_s to the workspace; a second kernel
+ * combines them exactly:
+ *
+ *     LSE = log sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s
+ *
+ * (the recurrence of page "22. GPU Engineering: Correctness, Throughput, and
+ * Attention", sec. 22.5, applied once to whole key ranges).  The split count
+ * is chosen from the sizes alone (about 1024 workgroups, >= 4 key tiles of 64
+ * per split), so results are deterministic for given sizes.
+ *
+ *   workspace       : device, 256-byte aligned, >= attn_fwd_split_workspace_size
+ *                     bytes (TA_ERR_INVALID_ARG if smaller, TA_ERR_MISALIGNED if
+ *                     misaligned); owned by the caller, overwritten.  May be
+ *                     NULL when that size is 0.  Concurrent calls need
+ *                     separate workspaces.
+ *   scale <= 0      : runs unsplit (as attn_fwd_ex).
+ *   everything else : as for attn_fwd_ex.
+ */
+int attn_fwd_split(const void* q, const void* k, const void* v, float* o, float* lse, int B,
+                   int H, int Nq, int Nk, int d, int dv, int query_offset, float scale, int causal,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * attn_fwd_dropout -- attn_fwd with dropout on the probabilities (page
  * "22. GPU Engineering: Correctness, Throughput, and Attention", sec. 22.5:
  * dropout only with reproducible masks).  For head n = b * H + h, query row i

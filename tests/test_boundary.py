@@ -44,6 +44,7 @@ def test_header_declares_entry_points():
                                     "attn_bwd_workspace_size",
                                     "attn_fwd",
                                     "attn_fwd_dropout", "attn_fwd_ex", "attn_fwd_fp8",
+                                    "attn_fwd_split", "attn_fwd_split_workspace_size",
                                     "attn_quantize_fp8", "attn_status_string"]
 
 
@@ -370,3 +371,51 @@ def test_bwd_square_entry_still_rejects_empty():
     lib = ta.load_library()
     assert ta.attn_bwd_raw(*([A] * 10), 1, 2, 0, 128, 0.1, 1, 0) == ta.TA_ERR_INVALID_ARG
     assert lib.attn_bwd_workspace_size(1, 2, 0) == 0
+
+
+# ---- split-key forward ----------------------------------------------------------
+
+def test_split_plan_sizes():
+    ws = ta.attn_fwd_split_workspace_size
+    assert ws(2, 8, 16, 32768, 128) > 0              # 16 workgroups: split
+    assert ws(16, 32, 1, 8192, 128) > 0              # 512 workgroups: split in two
+    assert ws(2, 32, 8192, 8192, 128) == 0           # 4096 workgroups: no split
+    assert ws(1, 1, 1, 300, 128) == 0                # fewer than 8 key tiles
+    assert ws(1, 1, 0, 4096, 128) == 0               # no queries
+    assert ws(0, 1, 1, 4096, 128) == 0 and ws(1, 1, 1, 4096, 96) == 0   # out of range
+    # partial O (dv floats) and LSE per (split, row), each part 256-byte aligned
+    n = ws(2, 8, 16, 32768, 64)
+    assert n % 256 == 0 and n >= 2 * 8 * 16 * 65 * 4
+
+
+SPLIT_PTRS = ["q", "k", "v", "o", "lse"]
+
+
+def call_split(ws=A, ws_bytes=1 << 30, **over):
+    args = dict({p: A for p in SPLIT_PTRS}, B=2, H=8, Nq=16, Nk=32768, d=128, dvw=128, off=32752,
+                scale=0.09, causal=1)
+    args.update(over)
+    return ta.attn_fwd_split_raw(*(args[p] for p in SPLIT_PTRS), args["B"], args["H"], args["Nq"],
+                                 args["Nk"], args["d"], args["dvw"], args["off"], args["scale"],
+                                 args["causal"], ws, ws_bytes, 0)
+
+
+@host_only
+def test_split_workspace_checks():
+    need = ta.attn_fwd_split_workspace_size(2, 8, 16, 32768, 128)
+    assert call_split(ws=0) == ta.TA_ERR_INVALID_ARG
+    assert call_split(ws_bytes=need - 1) == ta.TA_ERR_INVALID_ARG
+    assert call_split(ws=A + 128) == ta.TA_ERR_MISALIGNED
+
+
+@host_only
+@pytest.mark.parametrize("over", [dict(Nq=-1), dict(off=-5), dict(causal=2), dict(q=0),
+                                  dict(scale=math.inf)])
+def test_split_invalid(over):
+    assert call_split(**over) == ta.TA_ERR_INVALID_ARG
+
+
+@host_only
+def test_split_head_dims_and_alignment():
+    assert call_split(d=32) == ta.TA_ERR_UNSUPPORTED
+    assert call_split(o=A + 8) == ta.TA_ERR_MISALIGNED

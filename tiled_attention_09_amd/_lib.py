@@ -51,6 +51,11 @@ def load_library() -> ctypes.CDLL:
         lib.attn_fwd_dropout.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p]
         lib.attn_fwd_dropout.restype = ctypes.c_int
+        lib.attn_fwd_split_workspace_size.argtypes = [ctypes.c_int] * 5
+        lib.attn_fwd_split_workspace_size.restype = ctypes.c_size_t
+        lib.attn_fwd_split.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 7 + [
+            ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        lib.attn_fwd_split.restype = ctypes.c_int
         lib.attn_bwd_ex.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 7 + [
             ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
         lib.attn_bwd_ex.restype = ctypes.c_int
@@ -211,6 +216,60 @@ def attn_fwd_ex(q, k, v, scale: float | None = None, causal: bool = False, query
                          int(bool(causal)), int(stream))
     if st != TA_OK:
         raise RuntimeError("attn_fwd_ex failed: %s (status %d)" % (attn_status_string(st), st))
+    return out, lse
+
+
+def attn_fwd_split_workspace_size(B: int, H: int, Nq: int, Nk: int, dv: int) -> int:
+    """Bytes of device workspace ``attn_fwd_split`` uses (0: it runs unsplit)."""
+    return int(load_library().attn_fwd_split_workspace_size(B, H, Nq, Nk, dv))
+
+
+def attn_fwd_split_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int,
+                       H: int, Nq: int, Nk: int, d: int, dv: int, query_offset: int, scale: float,
+                       causal: int, ws_ptr: int, ws_bytes: int, stream: int = 0) -> int:
+    """Call the split-key forward's C entry point with raw addresses; returns the status."""
+    return load_library().attn_fwd_split(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Nq, Nk, d, dv,
+                                         query_offset, ctypes.c_float(scale), causal, ws_ptr,
+                                         ws_bytes, stream)
+
+
+def attn_fwd_split(q, k, v, scale: float | None = None, causal: bool = False,
+                   query_offset: int = 0, out=None, lse=None, workspace=None, stream=None):
+    """``attn_fwd_ex`` with the key range split over workgroups when the
+    (head, query tile) grid is small (decoding over long contexts); the partial
+    results are combined exactly by their log-normalisers.  ``workspace`` (a
+    uint8 device tensor of ``attn_fwd_split_workspace_size`` bytes) is
+    allocated here when not given.  Returns (o, lse)."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or t.dtype != torch.bfloat16 or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous bfloat16 device tensor [B, H, rows, width]"
+                             % name)
+    B, H, Nq, d = (int(x) for x in q.shape)
+    if tuple(k.shape[:2]) != (B, H) or int(k.shape[3]) != d or tuple(v.shape[:3]) != tuple(k.shape[:3]):
+        raise ValueError("k must be [B, H, Nk, d] and v [B, H, Nk, dv]")
+    Nk, dv = int(k.shape[2]), int(v.shape[3])
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, Nq, dv), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if out.shape != (B, H, Nq, dv) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be contiguous float32 [B, H, Nq, dv]")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, Nq]")
+    need = attn_fwd_split_workspace_size(B, H, Nq, Nk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = load_library().attn_fwd_split(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Nq, Nk, d,
+        dv, int(query_offset), ctypes.c_float(float(scale)), int(bool(causal)), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), int(stream))
+    if st != TA_OK:
+        raise RuntimeError("attn_fwd_split failed: %s (status %d)" % (attn_status_string(st), st))
     return out, lse
 
 

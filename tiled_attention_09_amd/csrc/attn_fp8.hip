@@ -26,10 +26,10 @@ int launch_fp8(const void* q8, const void* k8, const void* v, float* o, float* l
   const uint16_t* vv = static_cast<const uint16_t*>(v);
   if (scale_log2 > 0.f)
     tiledattn::attn_fwd_kernel<128, 128, CAUSAL, true, false, true><<<grid, block, 0, stream>>>(
-        q8, k8, vv, o, lse, bh, N, N, 0, n_qt, scale_log2, qd, kd, tiledattn::DropoutArgs{});
+        q8, k8, vv, o, lse, bh, N, N, 0, n_qt, scale_log2, qd, kd, tiledattn::DropoutArgs{}, bh, 0);
   else
     tiledattn::attn_fwd_kernel<128, 128, CAUSAL, false, false, true><<<grid, block, 0, stream>>>(
-        q8, k8, vv, o, lse, bh, N, N, 0, n_qt, scale_log2, qd, kd, tiledattn::DropoutArgs{});
+        q8, k8, vv, o, lse, bh, N, N, 0, n_qt, scale_log2, qd, kd, tiledattn::DropoutArgs{}, bh, 0);
   return hipGetLastError() == hipSuccess ? TA_OK : TA_ERR_HIP;
 }
 

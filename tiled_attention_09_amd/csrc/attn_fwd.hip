@@ -39,22 +39,22 @@ int launch(const void* q, const void* k, const void* v, float* o, float* lse, in
       if (scale_log2 > 0.f)
         tiledattn::attn_fwd_kernel<D, D, CAUSAL, true, false, false, true>
             <<<grid, block, 0, stream>>>(qq, kk, vv, o, lse, bh, Nq, Nk, 0, n_qt, scale_log2,
-                                         nullptr, nullptr, *dr);
+                                         nullptr, nullptr, *dr, bh, 0);
       else
         tiledattn::attn_fwd_kernel<D, D, CAUSAL, false, false, false, true>
             <<<grid, block, 0, stream>>>(qq, kk, vv, o, lse, bh, Nq, Nk, 0, n_qt, scale_log2,
-                                         nullptr, nullptr, *dr);
+                                         nullptr, nullptr, *dr, bh, 0);
       return hipGetLastError() == hipSuccess ? TA_OK : TA_ERR_HIP;
     }
   }
   if (scale_log2 > 0.f)
     tiledattn::attn_fwd_kernel<D, DV, CAUSAL, true, GENERAL><<<grid, block, 0, stream>>>(
         qq, kk, vv, o, lse, bh, Nq, Nk, offset, n_qt, scale_log2, nullptr, nullptr,
-        tiledattn::DropoutArgs{});
+        tiledattn::DropoutArgs{}, bh, 0);
   else
     tiledattn::attn_fwd_kernel<D, DV, CAUSAL, false, GENERAL><<<grid, block, 0, stream>>>(
         qq, kk, vv, o, lse, bh, Nq, Nk, offset, n_qt, scale_log2, nullptr, nullptr,
-        tiledattn::DropoutArgs{});
+        tiledattn::DropoutArgs{}, bh, 0);
   return hipGetLastError() == hipSuccess ? TA_OK : TA_ERR_HIP;
 }
 
@@ -67,12 +67,9 @@ int launch_mask(const void* q, const void* k, const void* v, float* o, float* ls
              : launch<D, DV, false, GENERAL>(q, k, v, o, lse, bh, Nq, Nk, offset, scale_log2, dr, s);
 }
 
-// Shared by attn_fwd (square = true: the instance with Nk = Nq and offset 0
-// fixed at compile time), attn_fwd_dropout (square, dr set) and attn_fwd_ex:
-// every check happens before any HIP call.
-int forward(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H,
-            int Nq, int Nk, int d, int dv, int offset, float scale, int causal, void* stream,
-            bool square, const tiledattn::DropoutArgs* dr = nullptr) {
+// Argument checks of every forward entry point, before any HIP call.
+int check(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H,
+          int Nq, int Nk, int d, int dv, int offset, float scale, int causal) {
   if (B < 1 || H < 1 || Nq < 0 || Nq > kMaxN || Nk < 0 || Nk > kMaxN) return TA_ERR_INVALID_ARG;
   // A pointer may be NULL only where its tensor is empty.
   if ((Nq > 0 && (!q || !o || !lse)) || (Nk > 0 && (!k || !v))) return TA_ERR_INVALID_ARG;
@@ -85,6 +82,17 @@ int forward(const void* q, const void* k, const void* v, float* o, float* lse, i
   const int64_t bh = (int64_t)B * H;
   const int64_t n_qt = (Nq + tiledattn::kBM - 1) / tiledattn::kBM;
   if (bh * n_qt > INT32_MAX) return TA_ERR_INVALID_ARG;
+  return TA_OK;
+}
+
+// Shared by attn_fwd (square = true: the instance with Nk = Nq and offset 0
+// fixed at compile time), attn_fwd_dropout (square, dr set) and attn_fwd_ex.
+int forward(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H,
+            int Nq, int Nk, int d, int dv, int offset, float scale, int causal, void* stream,
+            bool square, const tiledattn::DropoutArgs* dr = nullptr) {
+  const int st = check(q, k, v, o, lse, B, H, Nq, Nk, d, dv, offset, scale, causal);
+  if (st != TA_OK) return st;
+  const int64_t bh = (int64_t)B * H;
   if (Nq == 0) return TA_OK;                       // nothing to compute
 
   // Scores enter exp2: fold log2(e) into the scale once, in double.
@@ -107,7 +115,102 @@ int forward(const void* q, const void* k, const void* v, float* o, float* lse, i
                                                 causal, nullptr, s);
 }
 
+// Split key ranges (attn_fwd_split): when the (head, query tile) grid is too
+// small to fill the chip -- a decoding step of a few sequences over a long
+// context -- the keys are split over workgroups so that about kSplitTarget
+// workgroups stream K and V, each covering an even number (>= 4) of key tiles.
+constexpr int64_t kSplitTarget = 1024;
+
+struct SplitPlan {
+  int n_split, tiles;
+};
+
+SplitPlan plan_split(int64_t bh, int Nq, int Nk) {
+  const int64_t grid = bh * ((Nq + tiledattn::kBM - 1) / tiledattn::kBM);
+  const int n_kt = (Nk + tiledattn::kBN - 1) / tiledattn::kBN;
+  if (grid == 0 || grid >= kSplitTarget || n_kt < 8) return {1, n_kt};
+  const int64_t want = (kSplitTarget + grid - 1) / grid;
+  int n = (int)(want < n_kt / 4 ? want : n_kt / 4);
+  int tiles = (n_kt + n - 1) / n;
+  tiles += tiles & 1;
+  n = (n_kt + tiles - 1) / tiles;
+  return {n, tiles};
+}
+
+// Workspace of a split call: the partial O ([n_split][B H Nq][dv] fp32) and
+// LSE ([n_split][B H Nq]), each 256-byte aligned; 0 when no split is planned.
+size_t split_bytes(int64_t bh, int Nq, int dv, SplitPlan p) {
+  if (p.n_split <= 1) return 0;
+  const size_t rows = (size_t)p.n_split * (size_t)bh * (size_t)Nq;
+  return ((rows * (size_t)dv * 4u + 255u) & ~(size_t)255u) + ((rows * 4u + 255u) & ~(size_t)255u);
+}
+
+template <int D, int DV, bool CAUSAL>
+int launch_split(const void* q, const void* k, const void* v, float* o, float* lse, int bh,
+                 int Nq, int Nk, int offset, float scale_log2, SplitPlan p, float* ws,
+                 hipStream_t stream) {
+  const int n_qt = (Nq + tiledattn::kBM - 1) / tiledattn::kBM;
+  const int64_t rows = (int64_t)bh * Nq;
+  float* part_o = ws;
+  float* part_l = ws + ((((size_t)p.n_split * rows * DV * 4u + 255u) & ~(size_t)255u) / 4u);
+  tiledattn::attn_fwd_kernel<D, DV, CAUSAL, true, true, false, false, true>
+      <<<dim3((unsigned)(p.n_split * bh * n_qt)), dim3(tiledattn::kThreads), 0, stream>>>(
+          q, k, static_cast<const uint16_t*>(v), part_o, part_l, p.n_split * bh, Nq, Nk, offset,
+          n_qt, scale_log2, nullptr, nullptr, tiledattn::DropoutArgs{}, bh, p.tiles);
+  tiledattn::attn_split_merge_kernel<DV><<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream>>>(
+      part_o, part_l, o, lse, rows, p.n_split);
+  return hipGetLastError() == hipSuccess ? TA_OK : TA_ERR_HIP;
+}
+
+template <int D, int DV>
+int launch_split_mask(const void* q, const void* k, const void* v, float* o, float* lse, int bh,
+                      int Nq, int Nk, int offset, float scale_log2, int causal, SplitPlan p,
+                      float* ws, hipStream_t s) {
+  return causal ? launch_split<D, DV, true>(q, k, v, o, lse, bh, Nq, Nk, offset, scale_log2, p, ws, s)
+                : launch_split<D, DV, false>(q, k, v, o, lse, bh, Nq, Nk, offset, scale_log2, p, ws,
+                                             s);
+}
+
 }  // namespace
+
+extern "C" size_t attn_fwd_split_workspace_size(int B, int H, int Nq, int Nk, int dv) {
+  if (B < 1 || H < 1 || Nq < 0 || Nq > kMaxN || Nk < 0 || Nk > kMaxN) return 0;
+  if (dv != 64 && dv != 128) return 0;
+  const int64_t bh = (int64_t)B * H;
+  if (bh * ((Nq + tiledattn::kBM - 1) / tiledattn::kBM) > INT32_MAX) return 0;
+  return split_bytes(bh, Nq, dv, plan_split(bh, Nq, Nk));
+}
+
+extern "C" int attn_fwd_split(const void* q, const void* k, const void* v, float* o, float* lse,
+                              int B, int H, int Nq, int Nk, int d, int dv, int query_offset,
+                              float scale, int causal, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  const int st = check(q, k, v, o, lse, B, H, Nq, Nk, d, dv, query_offset, scale, causal);
+  if (st != TA_OK) return st;
+  const int64_t bh = (int64_t)B * H;
+  const SplitPlan p = plan_split(bh, Nq, Nk);
+  const size_t need = split_bytes(bh, Nq, dv, p);
+  // Without a split (or with a non-positive scale) this is attn_fwd_ex.
+  if (need == 0 || !(scale > 0.f))
+    return forward(q, k, v, o, lse, B, H, Nq, Nk, d, dv, query_offset, scale, causal, stream, false);
+  if (!workspace || workspace_bytes < need) return TA_ERR_INVALID_ARG;
+  if (!aligned(workspace, 256)) return TA_ERR_MISALIGNED;
+  if ((int64_t)p.n_split * bh * ((Nq + tiledattn::kBM - 1) / tiledattn::kBM) > INT32_MAX)
+    return TA_ERR_INVALID_ARG;
+  const float scale_log2 = (float)((double)scale * 1.4426950408889634073599);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* ws = static_cast<float*>(workspace);
+  const int ibh = (int)bh;
+  if (d == 64)
+    return dv == 64 ? launch_split_mask<64, 64>(q, k, v, o, lse, ibh, Nq, Nk, query_offset,
+                                                scale_log2, causal, p, ws, s)
+                    : launch_split_mask<64, 128>(q, k, v, o, lse, ibh, Nq, Nk, query_offset,
+                                                 scale_log2, causal, p, ws, s);
+  return dv == 64 ? launch_split_mask<128, 64>(q, k, v, o, lse, ibh, Nq, Nk, query_offset,
+                                               scale_log2, causal, p, ws, s)
+                  : launch_split_mask<128, 128>(q, k, v, o, lse, ibh, Nq, Nk, query_offset,
+                                                scale_log2, causal, p, ws, s);
+}
 
 extern "C" int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse, int B,
                         int H, int N, int d, float scale, int causal, void* stream) {

@@ -67,16 +67,22 @@ constexpr int kDropValuPerMfma = 16;
 // square shapes).  DROPOUT: each probability is kept or zeroed by the
 // reproducible mask of `drop` (DropoutArgs) and the output scaled by
 // keep_scale; the normaliser and LSE count every visible key (square shapes).
+// SPLIT: the key range is split over workgroups: bh_count counts (split,
+// head) pairs, workgroup (s, head) covers key tiles [s split_tiles,
+// (s + 1) split_tiles) and writes its own normalised O and LSE at index
+// s * heads + head of O and LSE (attn_split_merge_kernel combines them).
 template <int D, int DV, bool CAUSAL, bool POS_SCALE, bool GENERAL, bool F8 = false,
-          bool DROPOUT = false>
+          bool DROPOUT = false, bool SPLIT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
                      const uint16_t* __restrict__ V, float* __restrict__ O,
                      float* __restrict__ LSE, int bh_count, int Nq, int nk_arg, int offset_arg,
                      int n_qt, float scale_log2, const float* __restrict__ q_descale,
-                     const float* __restrict__ k_descale, DropoutArgs drop) {
+                     const float* __restrict__ k_descale, DropoutArgs drop, int heads,
+                     int split_tiles) {
   static_assert(!F8 || (D == 128 && DV == 128 && !GENERAL), "FP8 scores: d = 128, square");
   static_assert(!DROPOUT || (!GENERAL && !F8), "dropout: square bf16 shapes");
+  static_assert(!SPLIT || (GENERAL && !F8 && !DROPOUT), "split key ranges: general bf16 shapes");
   const int Nk = GENERAL ? nk_arg : Nq;
   const int offset = GENERAL ? offset_arg : 0;
   using T = Tile<D>;
@@ -98,8 +104,10 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  int bh, qt;
-  map_block(blockIdx.x, bh_count, n_qt, CAUSAL, bh, qt);
+  int bhs, qt;
+  map_block(blockIdx.x, bh_count, n_qt, CAUSAL, bhs, qt);
+  const int split = SPLIT ? bhs / heads : 0;
+  const int bh = SPLIT ? bhs - split * heads : bhs;   // (batch, head) of Q, K, V
 
   const __amdgpu_buffer_rsrc_t qr =
       make_rsrc(Q + (size_t)bh * Nq * D * kElemQK, (uint32_t)Nq * D * kElemQK);
@@ -152,7 +160,11 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
 
   // Key tiles this query tile can see (causal: up to its last row's position).
   const int n_kt_all = (Nk + kBN - 1) / kBN;
-  const int n_kt = CAUSAL ? min(n_kt_all, (qt * kBM + kBM + offset + kBN - 1) / kBN) : n_kt_all;
+  const int n_kt_vis = CAUSAL ? min(n_kt_all, (qt * kBM + kBM + offset + kBN - 1) / kBN) : n_kt_all;
+  // Key tiles of this workgroup: [kt_lo, n_kt) (kt_lo is even, so the stage
+  // parity of tile j is still j % 2).
+  const int kt_lo = SPLIT ? split * split_tiles : 0;
+  const int n_kt = SPLIT ? min(n_kt_vis, kt_lo + split_tiles) : n_kt_vis;
   const int q_last = q0 + 31 + offset;   // position of the wave's last query row
 
   // Tiles this wave takes part in: key tiles whose first key is not past the
@@ -335,16 +347,16 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
     }
   };
 
-  if (n_kt > 0) {
-    issue_rows<F8 ? 64 : D>(kr, src_k, 0, wave, (TA_LDS uint16_t*)k0);
-    issue_rows<DV>(vr, src_v, 0, wave, v0);
-    if (n_kt > 1) issue_rows<F8 ? 64 : D>(kr, src_k, 1, wave, (TA_LDS uint16_t*)k1);
+  if (n_kt > kt_lo) {
+    issue_rows<F8 ? 64 : D>(kr, src_k, kt_lo, wave, (TA_LDS uint16_t*)k0);
+    issue_rows<DV>(vr, src_v, kt_lo, wave, v0);
+    if (n_kt > kt_lo + 1) issue_rows<F8 ? 64 : D>(kr, src_k, kt_lo + 1, wave, (TA_LDS uint16_t*)k1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (n_w > 0) scores(k0, sa);
+    if (n_w > kt_lo) scores(k0, sa);
     if constexpr (DROPOUT) dropout_row_words((uint32_t)my_q, 0u, (uint32_t)bh, drop, hi, mw);
   }
-  for (int j = 0; j < n_kt; j += 2) {
+  for (int j = kt_lo; j < n_kt; j += 2) {
     iter(j, std::integral_constant<int, 0>{});
     if (j + 1 >= n_kt) break;
     iter(j + 1, std::integral_constant<int, 1>{});
@@ -357,7 +369,7 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
   if (my_q < Nq) {
     const bool live = l_row > 0.f;
     const float inv = live ? (DROPOUT ? drop.keep_scale : 1.f) / l_row : 0.f;
-    float* orow = O + ((size_t)bh * Nq + my_q) * DV;
+    float* orow = O + ((size_t)bhs * Nq + my_q) * DV;
 #pragma unroll
     for (int db = 0; db < TV::DB; ++db)
 #pragma unroll
@@ -368,8 +380,43 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
       }
     const float mlog2 = POS_SCALE ? m * scale_log2 : m;
     if (hi == 0)
-      LSE[(size_t)bh * Nq + my_q] = live ? (mlog2 + __log2f(l_row)) * kLn2 : -__builtin_inff();
+      LSE[(size_t)bhs * Nq + my_q] = live ? (mlog2 + __log2f(l_row)) * kLn2 : -__builtin_inff();
   }
+}
+
+// Combination of the partial results of a split key range, each normalised by
+// its own l: LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s (the
+// online-softmax recurrence of the tiles, applied once to whole key ranges).
+// Os: [n_split][rows][DV], Ls: [n_split][rows]; one wave per row.  A row
+// whose partial LSEs are all -inf saw no key: O = 0, LSE = -inf.
+template <int DV>
+__global__ __launch_bounds__(256) void attn_split_merge_kernel(const float* __restrict__ Os,
+                                                               const float* __restrict__ Ls,
+                                                               float* __restrict__ O,
+                                                               float* __restrict__ LSE,
+                                                               int64_t rows, int n_split) {
+  constexpr int C = DV / 64;   // output columns per lane
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  float m = -__builtin_inff();
+  for (int sp = 0; sp < n_split; ++sp) m = fmaxf(m, Ls[sp * rows + row]);
+  float acc[C] = {};
+  float den = 0.f;
+  if (m != -__builtin_inff()) {
+    for (int sp = 0; sp < n_split; ++sp) {
+      const float w = expf(Ls[sp * rows + row] - m);
+      den += w;
+      const float* src = Os + (sp * rows + row) * DV + lane * C;
+#pragma unroll
+      for (int c = 0; c < C; ++c) acc[c] = __builtin_fmaf(w, src[c], acc[c]);
+    }
+  }
+  const bool live = den > 0.f;
+  float* dst = O + row * DV + lane * C;
+#pragma unroll
+  for (int c = 0; c < C; ++c) dst[c] = live ? acc[c] / den : 0.f;
+  if (lane == 0) LSE[row] = live ? m + logf(den) : -__builtin_inff();
 }
 
 }  // namespace tiledattn
