@@ -117,9 +117,15 @@ int forward(const void* q, const void* k, const void* v, float* o, float* lse, i
 
 // Split key ranges (attn_fwd_split): when the (head, query tile) grid is too
 // small to fill the chip -- a decoding step of a few sequences over a long
-// context -- the keys are split over workgroups so that about kSplitTarget
-// workgroups stream K and V, each covering an even number (>= 4) of key tiles.
-constexpr int64_t kSplitTarget = 1024;
+// context -- the keys are split over workgroups, each covering an even number
+// (>= 4) of key tiles.  Grids below one workgroup per compute unit are split
+// up to kSplitFill workgroups (one per CU streaming a long key range measured
+// best: 16 queries over 32768 keys in 16 heads reached 5.2 TB/s with 256
+// workgroups, 4.5 with 512, 3.6 with 1024, 3.7 with 128); grids below
+// kSplitTwo are split in two (a 1024-query chunk over 8192 keys in 64 heads:
+// 9 % faster).
+constexpr int64_t kSplitFill = 256;
+constexpr int64_t kSplitTwo = 1024;
 
 struct SplitPlan {
   int n_split, tiles;
@@ -128,8 +134,8 @@ struct SplitPlan {
 SplitPlan plan_split(int64_t bh, int Nq, int Nk) {
   const int64_t grid = bh * ((Nq + tiledattn::kBM - 1) / tiledattn::kBM);
   const int n_kt = (Nk + tiledattn::kBN - 1) / tiledattn::kBN;
-  if (grid == 0 || grid >= kSplitTarget || n_kt < 8) return {1, n_kt};
-  const int64_t want = (kSplitTarget + grid - 1) / grid;
+  if (grid == 0 || grid >= kSplitTwo || n_kt < 8) return {1, n_kt};
+  const int64_t want = grid < kSplitFill ? (kSplitFill + grid - 1) / grid : 2;
   int n = (int)(want < n_kt / 4 ? want : n_kt / 4);
   int tiles = (n_kt + n - 1) / n;
   tiles += tiles & 1;
