@@ -9,6 +9,10 @@
 // each block of P is rebuilt as exp(S - LSE).  Base-2 exponentials: with
 // c = scale log2(e) and LSE2 = LSE log2(e), P = 2^(c (q.k) - LSE2).
 //
+// Shapes: Nq query rows at positions offset .. offset + Nq - 1 and Nk keys
+// per head (the square case Nq = Nk, offset 0 has instances of its own); Q
+// and K rows of width D, V, O and G rows of width DV.
+//
 // Three kernels, all on the caller's stream:
 //  1. attn_bwd_prep_kernel: per row, D and LSE2 into a workspace of float2
 //     {LSE2, D}, each head's rows padded to an even count so every head starts

@@ -46,6 +46,9 @@
 //  * General shapes: Nq queries and Nk keys per head, Q/K rows of width D and
 //    V/O rows of width DV; with no keys a row keeps l = 0 and gets O = 0,
 //    LSE = -inf (the lab's fully-hidden-row policy).
+//  * Split key ranges (decoding over long contexts): workgroups cover key
+//    tile ranges of one (head, query tile) and write their own normalised O
+//    and LSE; attn_split_merge_kernel combines them by their log-normalisers.
 #pragma once
 
 #include "attn_common.hpp"
