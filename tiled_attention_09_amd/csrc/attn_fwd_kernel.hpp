@@ -271,24 +271,36 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
     return alpha;
   };
 
-  // O^T (dv x 32 queries) += V^T (dv x 64 keys) P^T (64 keys x 32 queries).
-  // With dropout, the mask words of tile j + 1 are generated meanwhile (the
-  // vector unit is otherwise idle during these products).
-  auto values = [&](int j, const TA_LDS uint16_t* vt, const bf16x8 (&pf)[4])
+  // o = alpha o, then O^T (dv x 32 queries) += V^T (dv x 64 keys) P^T (64 keys
+  // x 32 queries).  The transposed V operands of the first four products are
+  // read before the rescale, so that when some row moved its maximum the 16 DV
+  // / 32 multiplies per block run under the latency of those reads instead of
+  // ahead of them.  With dropout, the mask words of tile j + 1 are generated
+  // meanwhile (the vector unit is otherwise idle during these products).
+  auto values = [&](int j, const TA_LDS uint16_t* vt, const bf16x8 (&pf)[4], float alpha)
                     __attribute__((always_inline)) {
+    bf16x8 vpre[TV::DB];
+#pragma unroll
+    for (int db = 0; db < TV::DB; ++db) vpre[db] = rdv.col_op(vt, 0, db);
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < TV::DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    }
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
       for (int db = 0; db < TV::DB; ++db)
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rdv.col_op(vt, g, db), pf[g], oacc[db],
-                                                           0, 0, 0);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            g == 0 ? vpre[db] : rdv.col_op(vt, g, db), pf[g], oacc[db], 0, 0, 0);
     if constexpr (DROPOUT) {
       dropout_row_words((uint32_t)my_q, (uint32_t)(j + 1), (uint32_t)bh, drop, hi, mw);
-      sched_mfma_ds_valu<8, 2, 8 * TV::DB, kDropValuPerMfma>(
+      sched_mfma_ds_valu<0, 2, 6 * TV::DB, kDropValuPerMfma>(
           std::make_integer_sequence<int, 4 * TV::DB>{});
     } else {
-      // Eight transposed V reads in flight, then two more per product.
-      sched_mfma_ds<8, 2, 8 * TV::DB>(std::make_integer_sequence<int, 4 * TV::DB>{});
+      // The remaining reads, two after each product (eight in flight).
+      sched_mfma_ds<0, 2, 6 * TV::DB>(std::make_integer_sequence<int, 4 * TV::DB>{});
     }
   };
 
@@ -326,13 +338,7 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
     // exponentials below the rescale branch, out of reach of the interleave.
     asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(pf[2]), "v"(pf[3]));
     __builtin_amdgcn_s_setprio(0);
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-      for (int db = 0; db < TV::DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-    }
-    values(j, v_cur, pf);
+    values(j, v_cur, pf, alpha);
   };
   // Iteration j with the stage parity P = j % 2 fixed at compile time.
   auto iter = [&](int j, auto pc) __attribute__((always_inline)) {
