@@ -272,16 +272,19 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
   };
 
   // o = alpha o, then O^T (dv x 32 queries) += V^T (dv x 64 keys) P^T (64 keys
-  // x 32 queries).  The transposed V operands of the first four products are
-  // read before the rescale, so that when some row moved its maximum the 16 DV
-  // / 32 multiplies per block run under the latency of those reads instead of
-  // ahead of them.  With dropout, the mask words of tile j + 1 are generated
-  // meanwhile (the vector unit is otherwise idle during these products).
+  // x 32 queries).  Without dropout the transposed V operands of the first
+  // four products are read before the rescale, so that when some row moved
+  // its maximum the 16 DV / 32 multiplies per block run under the latency of
+  // those reads instead of ahead of them.  With dropout (whose mask generator
+  // needs those registers) the reads follow the rescale, and the mask words
+  // of tile j + 1 are generated during the products (the vector unit is
+  // otherwise idle there).
   auto values = [&](int j, const TA_LDS uint16_t* vt, const bf16x8 (&pf)[4], float alpha)
                     __attribute__((always_inline)) {
+    constexpr int NPRE = DROPOUT ? 0 : TV::DB;   // operands read before the rescale
     bf16x8 vpre[TV::DB];
 #pragma unroll
-    for (int db = 0; db < TV::DB; ++db) vpre[db] = rdv.col_op(vt, 0, db);
+    for (int db = 0; db < NPRE; ++db) vpre[db] = rdv.col_op(vt, 0, db);
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
       for (int db = 0; db < TV::DB; ++db)
@@ -293,10 +296,11 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
 #pragma unroll
       for (int db = 0; db < TV::DB; ++db)
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            g == 0 ? vpre[db] : rdv.col_op(vt, g, db), pf[g], oacc[db], 0, 0, 0);
+            (g == 0 && NPRE) ? vpre[db] : rdv.col_op(vt, g, db), pf[g], oacc[db], 0, 0, 0);
     if constexpr (DROPOUT) {
       dropout_row_words((uint32_t)my_q, (uint32_t)(j + 1), (uint32_t)bh, drop, hi, mw);
-      sched_mfma_ds_valu<0, 2, 6 * TV::DB, kDropValuPerMfma>(
+      // Eight transposed V reads in flight, then two more per product.
+      sched_mfma_ds_valu<8, 2, 8 * TV::DB, kDropValuPerMfma>(
           std::make_integer_sequence<int, 4 * TV::DB>{});
     } else {
       // The remaining reads, two after each product (eight in flight).
