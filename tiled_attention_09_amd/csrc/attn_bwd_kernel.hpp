@@ -392,7 +392,18 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 
   // Epilogue: lane owns key my_k; accumulator element e of block db is column
   // 32 db + 8 (e / 4) + 4 hi + e % 4.
-  if (my_k < Nk) {
+  const float vs = DROPOUT ? drop.keep_scale : 1.f;
+  if constexpr (D == DV) {
+    // dK, then dV, through LDS (store_rows_lds): each wave uses one of the
+    // now free Q/G stages.
+    __syncthreads();                       // every wave is done with the stages
+    TA_LDS uint8_t* const reg = wave == 0 ? (TA_LDS uint8_t*)q_lds0
+                                : wave == 1 ? (TA_LDS uint8_t*)g_lds0
+                                : wave == 2 ? (TA_LDS uint8_t*)q_lds1
+                                            : (TA_LDS uint8_t*)g_lds1;
+    store_rows_lds<D>(reg, dk, scale, dK + (khead + k0) * D, Nk - k0, lane);
+    store_rows_lds<DV>(reg, dv, vs, dV + (khead + k0) * DV, Nk - k0, lane);
+  } else if (my_k < Nk) {
     float* dkrow = dK + (khead + my_k) * D;
     float* dvrow = dV + (khead + my_k) * DV;
     constexpr int DBM = T::DB > TG::DB ? T::DB : TG::DB;
@@ -406,7 +417,6 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
           *reinterpret_cast<f32x4*>(dkrow + db * 32 + 8 * g + 4 * hi) = a;
         }
         if (db < TG::DB) {
-          const float vs = DROPOUT ? drop.keep_scale : 1.f;
           f32x4 b = {dv[db][4 * g] * vs, dv[db][4 * g + 1] * vs, dv[db][4 * g + 2] * vs,
                      dv[db][4 * g + 3] * vs};
           *reinterpret_cast<f32x4*>(dvrow + db * 32 + 8 * g + 4 * hi) = b;
@@ -569,7 +579,16 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     if (active(j + 1)) compute_tile(j + 1, k1p, v1p);
   }
 
-  if (my_q < Nq) {
+  if constexpr (DV >= D) {
+    // dQ through LDS (store_rows_lds): each wave uses one of the now free
+    // K/V stages.
+    __syncthreads();                       // every wave is done with the stages
+    TA_LDS uint8_t* const reg = wave == 0 ? (TA_LDS uint8_t*)k0p
+                                : wave == 1 ? (TA_LDS uint8_t*)v0p
+                                : wave == 2 ? (TA_LDS uint8_t*)k1p
+                                            : (TA_LDS uint8_t*)v1p;
+    store_rows_lds<D>(reg, dq, scale, dQ + (qhead + q0) * D, Nq - q0, lane);
+  } else if (my_q < Nq) {
     float* row = dQ + (qhead + my_q) * D;
 #pragma unroll
     for (int db = 0; db < T::DB; ++db)

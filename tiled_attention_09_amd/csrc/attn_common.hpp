@@ -121,6 +121,43 @@ __device__ __forceinline__ void sched_rep() {
   sched_rep_impl<R, V>(std::make_integer_sequence<int, N>{});
 }
 
+// Store a wave's block of 32 rows x W fp32 results held as 32x32 MFMA
+// accumulators (acc[db][4 g + e] is row l32, column 32 db + 8 g + 4 hi + e),
+// each row scaled by the lane's s, to global rows blk + r W for r < rows.
+// Direct stores from that layout would write 32 bytes into each of 32 rows
+// per instruction; instead the block goes through the wave's own LDS region
+// reg (32 W 4 bytes) -- chunk c of row r at chunk slot c ^ (r mod W/4),
+// conflict-free for the row-wise reads -- and is read back row-contiguous,
+// so every store instruction writes whole rows (1 KiB).  The region must not
+// be in use by any other wave.
+template <int W>
+__device__ __forceinline__ void store_rows_lds(TA_LDS uint8_t* reg, const f32x16* acc, float s,
+                                               float* blk, int rows, int lane) {
+  constexpr int CH = W / 4;             // 16-byte chunks per row
+  constexpr uint32_t ROW = W * 4;       // bytes per row
+  const int l32 = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < W / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 val = {acc[db][4 * g] * s, acc[db][4 * g + 1] * s, acc[db][4 * g + 2] * s,
+                         acc[db][4 * g + 3] * s};
+      const int c = 8 * db + 2 * g + hi;  // chunk of columns 32 db + 8 g + 4 hi + [0, 4)
+      *reinterpret_cast<TA_LDS f32x4*>(reg + l32 * ROW + ((c ^ (l32 & (CH - 1))) << 4)) = val;
+    }
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int k = 0; k < (int)(32 * ROW / 1024); ++k) {
+    const uint32_t f = (uint32_t)k * 1024u + (uint32_t)lane * 16u;
+    const int r = (int)(f / ROW);
+    const int c = (int)((f % ROW) >> 4);
+    const f32x4 val =
+        *reinterpret_cast<const TA_LDS f32x4*>(reg + r * ROW + ((c ^ (r & (CH - 1))) << 4));
+    if (r < rows) *reinterpret_cast<f32x4*>(blk + (size_t)r * W + 4 * c) = val;
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
 // Workgroup -> (head, row tile).  Workgroups are handed to the 8 XCDs
 // round-robin, so block b runs on XCD b % 8; consecutive logical indices are
 // given to the same XCD so one head's tiles share that XCD's L2.  With

@@ -382,39 +382,14 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
   const bool live = l_row > 0.f;
   const float inv = live ? (DROPOUT ? drop.keep_scale : 1.f) / l_row : 0.f;
   if constexpr (!F8 && D >= DV) {
-    // O goes out through LDS: a lane holds 16-byte pieces of one row, so
-    // direct stores would write 32 bytes into each of 32 rows per instruction.
-    // Each wave writes its 32 x DV block into one of the (now free) K/V stages
-    // -- chunk c of row r at chunk slot c ^ (r mod CH), conflict-free for the
-    // row-wise reads -- and reads it back row-contiguous, so each store
-    // instruction writes whole rows (1 KiB per instruction).
-    constexpr int CH = DV / 4;              // 16-byte chunks per O row
-    constexpr uint32_t ROW = DV * 4;        // bytes per O row
+    // O goes out through LDS (store_rows_lds), each wave through one of the
+    // now free K/V stages.
     __syncthreads();                        // every wave is done with the stages
     TA_LDS uint8_t* const reg = wave == 0 ? k0
                                 : wave == 1 ? (TA_LDS uint8_t*)v0
                                 : wave == 2 ? k1
                                             : (TA_LDS uint8_t*)v1;
-#pragma unroll
-    for (int db = 0; db < TV::DB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 val = {oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv,
-                           oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv};
-        const int c = 8 * db + 2 * g + hi;  // chunk of columns db 32 + 8 g + 4 hi + [0, 4)
-        *reinterpret_cast<TA_LDS f32x4*>(reg + l32 * ROW + ((c ^ (l32 & (CH - 1))) << 4)) = val;
-      }
-    __builtin_amdgcn_wave_barrier();
-    float* const oblk = O + ((size_t)bhs * Nq + q0) * DV;
-#pragma unroll
-    for (int k = 0; k < (int)(32 * ROW / 1024); ++k) {
-      const uint32_t f = (uint32_t)k * 1024u + (uint32_t)lane * 16u;
-      const int r = (int)(f / ROW);
-      const int c = (int)((f % ROW) >> 4);
-      const f32x4 val =
-          *reinterpret_cast<const TA_LDS f32x4*>(reg + r * ROW + ((c ^ (r & (CH - 1))) << 4));
-      if (q0 + r < Nq) *reinterpret_cast<f32x4*>(oblk + (size_t)r * DV + 4 * c) = val;
-    }
+    store_rows_lds<DV>(reg, oacc, inv, O + ((size_t)bhs * Nq + q0) * DV, Nq - q0, lane);
   } else {
     if (my_q < Nq) {
       float* orow = O + ((size_t)bhs * Nq + my_q) * DV;
