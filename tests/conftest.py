@@ -9,4 +9,4 @@ for p in (ROOT, HERE):
 
 
 def pytest_configure(config):
-    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU; run on the GPU box")
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
