@@ -192,7 +192,7 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   const int hi = lane >> 5;
 
   int bh, kt;
-  map_block(blockIdx.x, bh_count, n_kt, false, bh, kt);   // causal: key tile 0 (most work) first
+  map_block(blockIdx.x, bh_count, n_kt, false, CAUSAL, 32, bh, kt);   // causal: key tile 0 has most work
 
   const size_t qhead = (size_t)bh * (size_t)Nq, khead = (size_t)bh * (size_t)Nk;
   const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + qhead * D, (uint32_t)Nq * D * 2u);
@@ -454,7 +454,7 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   const int hi = lane >> 5;
 
   int bh, qt;
-  map_block(blockIdx.x, bh_count, n_qt, CAUSAL, bh, qt);
+  map_block(blockIdx.x, bh_count, n_qt, CAUSAL, CAUSAL, 64, bh, qt);
 
   const size_t qhead = (size_t)bh * (size_t)Nq, khead = (size_t)bh * (size_t)Nk;
   const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + qhead * D, (uint32_t)Nq * D * 2u);

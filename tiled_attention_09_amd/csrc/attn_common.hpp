@@ -159,17 +159,35 @@ __device__ __forceinline__ void store_rows_lds(TA_LDS uint8_t* reg, const f32x16
 }
 
 // Workgroup -> (head, row tile).  Workgroups are handed to the 8 XCDs
-// round-robin, so block b runs on XCD b % 8; consecutive logical indices are
-// given to the same XCD so one head's tiles share that XCD's L2.  With
-// `reverse` the tiles of a head are taken last to first (causal query tiles:
-// the longest go first).
+// round-robin, so block b runs on XCD b % 8; each XCD is given a contiguous
+// eighth of the (head, tile) items, so one head's tiles share that XCD's L2.
+// With `reverse` the tiles of a head are taken last to first (causal query
+// tiles: the last has the most work).  An XCD normally takes its items head
+// by head.  When the work per tile changes monotonically with the tile index
+// (`monotone`: causal) and a head has fewer tiles than the XCD runs
+// workgroups at once (`slots`: 32 CUs times the workgroups per CU), the
+// last heads' longest tiles would start near the end of the queue and
+// stretch the tail (16 heads of 16 causal query tiles per XCD: a
+// list-scheduling makespan 1.26 times the even share), so the XCD then takes
+// tile position t of every one of its heads before position t + 1 (measured
+// 9 % faster forward, 8 % faster backward at B=8, H=16, N=2048).  With more
+// tiles per head both orders schedule evenly, and head by head keeps fewer
+// heads' K and V in L2 at once.
 __device__ __forceinline__ void map_block(int bid, int bh_count, int n_t, bool reverse,
-                                          int& bh, int& t_out) {
-  const int total = bh_count * n_t;
-  int j = bid;
-  if ((total & 7) == 0) j = (bid & 7) * (total >> 3) + (bid >> 3);
-  bh = j / n_t;
-  const int t = j - bh * n_t;
+                                          bool monotone, int slots, int& bh, int& t_out) {
+  int t;
+  if (monotone && n_t < slots && (bh_count & 7) == 0) {
+    const int hc = bh_count >> 3;         // heads per XCD
+    const int i = bid >> 3;               // position in this XCD's queue
+    bh = (bid & 7) * hc + i % hc;
+    t = i / hc;
+  } else {
+    const int total = bh_count * n_t;
+    int j = bid;
+    if ((total & 7) == 0) j = (bid & 7) * (total >> 3) + (bid >> 3);
+    bh = j / n_t;
+    t = j - bh * n_t;
+  }
   t_out = reverse ? n_t - 1 - t : t;
 }
 

@@ -108,7 +108,7 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
   const int hi = lane >> 5;
 
   int bhs, qt;
-  map_block(blockIdx.x, bh_count, n_qt, CAUSAL, bhs, qt);
+  map_block(blockIdx.x, bh_count, n_qt, CAUSAL, CAUSAL, 64, bhs, qt);
   const int split = SPLIT ? bhs / heads : 0;
   const int bh = SPLIT ? bhs - split * heads : bhs;   // (batch, head) of Q, K, V
 
