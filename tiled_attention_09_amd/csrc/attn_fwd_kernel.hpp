@@ -56,7 +56,7 @@
 namespace tiledattn {
 
 // Vector instructions of the softmax placed after each score product.
-constexpr int kValuPerMfma = 7;
+constexpr int kValuPerMfma = 5;
 // Vector instructions of the dropout generator placed after each value product.
 constexpr int kDropValuPerMfma = 16;
 
