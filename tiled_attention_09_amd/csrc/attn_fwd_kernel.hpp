@@ -55,8 +55,10 @@
 
 namespace tiledattn {
 
-// Vector instructions of the softmax placed after each score product.
+// Vector instructions of the softmax placed after each score product (square
+// shapes; the general-shape instances keep 7, with which they do not spill).
 constexpr int kValuPerMfma = 5;
+constexpr int kValuPerMfmaGeneral = 7;
 // Vector instructions of the dropout generator placed after each value product.
 constexpr int kDropValuPerMfma = 16;
 
@@ -203,7 +205,7 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
   // Score products per tile and the LDS reads that feed them.
   constexpr int kScoreMfma = F8 ? 2 * KS8 : 2 * T::KS;
   constexpr int kScoreReads = F8 ? 2 * kScoreMfma : kScoreMfma;
-  constexpr int kValuPerScore = F8 ? 16 : kValuPerMfma;
+  constexpr int kValuPerScore = F8 ? 16 : (GENERAL ? kValuPerMfmaGeneral : kValuPerMfma);
 
   // Scale (non-positive scales only) and hide future / non-existent keys of key
   // tile j in s; only tiles crossing the diagonal or the end of the keys need
