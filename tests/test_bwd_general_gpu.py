@@ -67,6 +67,9 @@ CASES = {  # name: (B, H, Nq, Nk, d, dv, offset, causal, mult, scale)
     "chunk_large_logits": (1, 2, 200, 700, 128, 128, 500, True, 4.0, None),
     "chunk_negative_scale": (1, 2, 130, 390, 64, 128, 260, True, 4.0, -0.125),
     "ragged_noncausal_dv64": (2, 2, 129, 191, 128, 64, 0, False, 1.0, None),
+    # 8 heads with few query and key tiles: causal tiles taken longest first across heads
+    "chunk_300_of_1200_8heads": (2, 4, 300, 1200, 128, 128, 900, True, 1.0, None),
+    "chunk_200_of_600_8heads_d64": (2, 4, 200, 600, 64, 64, 400, True, 1.0, None),
 }
 
 

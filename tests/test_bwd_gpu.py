@@ -108,6 +108,15 @@ def test_causal_mid(d, isolated):
     _check(got, ref, "causal N=700 d=%d" % d)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_causal_eight_heads_few_tiles(d):
+    # 8 heads and 6 tiles per head: the dQ and dK/dV grids take the XCDs'
+    # tiles longest first across heads (the order used below 64 / 32 tiles).
+    print("case bwd causal B=2,H=4,N=700,d=%d" % d, flush=True)
+    got, ref = _full_case(2, 4, 700, d, True, 31 + d, False)
+    _check(got, ref, "causal B=2,H=4,N=700 d=%d" % d)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [1, 2, 31, 33, 63, 64, 65, 127, 128, 129, 191, 255, 257])

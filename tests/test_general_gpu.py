@@ -69,6 +69,8 @@ CASES = {  # name: (B, H, Nq, Nk, d, dv, offset, causal, qk_mult, scale)
     "square_d128_dv64": (2, 3, 333, 333, 128, 64, 0, False, 1.0, None),
     "chunk_large_logits": (1, 2, 200, 700, 128, 128, 500, True, 4.0, None),
     "chunk_negative_scale": (1, 2, 130, 390, 64, 128, 260, True, 4.0, -0.125),
+    # 8 heads, 3 query tiles each: causal tiles taken longest first across heads
+    "chunk_300_of_1200_8heads": (2, 4, 300, 1200, 128, 128, 900, True, 1.0, None),
 }
 
 
