@@ -46,14 +46,18 @@ BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bwd_headline_traffic.jso
 
 
 def kernel_source_hash(names=FWD_SOURCES) -> str:
-    """sha256 over the HIP sources a kernel is built from (traffic figures are
-    only valid for the kernel they were measured on)."""
+    """sha256 over the HIP sources a kernel is built from, without their //
+    comments, trailing blanks and empty lines (traffic figures are only valid
+    for the kernel they were measured on; a comment edit does not change it)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tiled_attention_09_amd", "csrc")
     for name in sorted(names):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in f.read().splitlines())
+            code = "\n".join(ln for ln in lines if ln)
+        h.update(name.encode() + b"\0" + code.encode())
     return h.hexdigest()
 
 

@@ -28,10 +28,10 @@
 //    each, K one tile ahead of V; one barrier per tile.
 //  * Software pipeline inside the wave: while the softmax of tile j runs on
 //    the vector unit, the score products of tile j+1 run on the matrix unit
-//    (an explicit issue recipe interleaves them), then o is rescaled and
-//    P_j V_j accumulated.  The buffer range check returns zeros past the end of the head, so
-//    a ragged last tile needs no guard (zero V rows also keep 0 * garbage out
-//    of the sum).
+//    (an explicit issue recipe interleaves them), then o is rescaled (only
+//    when some row moved its maximum) and P_j V_j accumulated.  The buffer
+//    range check returns zeros past the end of the head, so a ragged last
+//    tile needs no guard (zero V rows also keep 0 * garbage out of the sum).
 //  * Both tiles keep the row-major [key][d] layout with the 16-byte chunks of
 //    each row XOR-swizzled by the row index.  K is read row-wise as the MFMA A
 //    operand (16 consecutive rows per 16 lanes hit 16 different chunk slots);
@@ -49,6 +49,8 @@
 //  * Split key ranges (decoding over long contexts): workgroups cover key
 //    tile ranges of one (head, query tile) and write their own normalised O
 //    and LSE; attn_split_merge_kernel combines them by their log-normalisers.
+//  * Epilogue: O leaves through LDS (store_rows_lds), so that each store
+//    instruction writes whole rows instead of 32-byte pieces of 32 rows.
 #pragma once
 
 #include "attn_common.hpp"
