@@ -19,12 +19,12 @@ Functions:
 
 * ``attention_bwd_ref`` -- that definition for one head: the full probability
   matrix from the two-pass softmax, and r from dP and P directly.
-* ``attention_bwd_tiled_ref`` -- the memory-saving method of sec. 22.7 in its
-  own steps: r taken through the output (the page shows
-  sum_j dP[i,j] P[i,j] = sum_c G[i,c] O[i,c]), each probability block
-  recomputed as exp(S - LSE) from the saved per-row log-normaliser, and the
-  three gradients accumulated block by block over a grid of query x key tiles.
-  It is pinned against the definition under many tilings.
+* ``attention_bwd_tiled_ref`` -- the memory-saving method of sec. 22.7: r
+  taken through the output (the page shows sum_j dP[i,j] P[i,j] =
+  sum_c G[i,c] O[i,c]) and each probability block recomputed as exp(S - LSE)
+  from the saved per-row log-normaliser, organised as two passes (key tiles
+  accumulate dK and dV, then query tiles accumulate dQ).  It is pinned against
+  the definition under many tilings.
 * ``attention_bwd_ref_batched`` -- the definition over [B, H, N, d] arrays,
   evaluating dQ only on chosen query rows and dK, dV only on chosen key rows
   (query rows are taken in chunks to bound memory; that only splits the sums
@@ -86,28 +86,49 @@ def attention_bwd_ref(q, k, v, do, scale: float, causal: bool = False, query_off
 
 def attention_bwd_tiled_ref(q, k, v, do, scale: float, q_bounds, k_bounds,
                             causal: bool = False, query_offset: int = 0):
-    """The recomputing backward of sec. 22.7 over query tiles [q_bounds[a], q_bounds[a+1])
-    times key tiles [k_bounds[b], k_bounds[b+1]).  Never forms more than one
-    probability block at a time."""
+    """The recomputing backward of sec. 22.7, organised in two passes over a grid
+    of query tiles [q_bounds[a], q_bounds[a+1]) and key tiles [k_bounds[b],
+    k_bounds[b+1]).  It keeps only the forward's per-row log-normaliser and
+    output, never the probability matrix:
+
+    * per row, the correction r_i = sum_c G[i,c] O[i,c] (the page's identity
+      for sum_j dP[i,j] P[i,j]);
+    * pass 1, one key tile at a time: its dK and dV rows are summed over every
+      query tile, each probability block rebuilt as exp(S - LSE);
+    * pass 2, one query tile at a time: its dQ rows are summed over every key
+      tile, rebuilding the same blocks.
+    At most one probability block exists at a time."""
     q, k, v, do = _as64(q, k, v, do)
     _check(q, k, v, do)
     out, lse = attention_ref(q, k, v, scale, causal, query_offset=query_offset)
-    r_all = np.einsum("ic,ic->i", do, out)          # sum_c G[i,c] O[i,c]
-    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
-    for q0, q1 in zip(q_bounds[:-1], q_bounds[1:]):
-        live = np.isfinite(lse[q0:q1])
-        log_norm = np.where(live, lse[q0:q1], 0.0)
-        qpos = np.arange(q0, q1) + query_offset
-        for k0, k1 in zip(k_bounds[:-1], k_bounds[1:]):
-            s = float(scale) * (q[q0:q1] @ k[k0:k1].T)
-            if causal:
-                s[np.arange(k0, k1)[None, :] > qpos[:, None]] = -np.inf
-            p = np.exp(s - log_norm[:, None])        # this block of P, rebuilt
-            p[~live] = 0.0
-            ds = p * (do[q0:q1] @ v[k0:k1].T - r_all[q0:q1, None])
-            dv[k0:k1] += p.T @ do[q0:q1]
-            dk[k0:k1] += float(scale) * (ds.T @ q[q0:q1])
-            dq[q0:q1] += float(scale) * (ds @ k[k0:k1])
+    r = (do * out).sum(axis=1)
+    q_tiles = list(zip(q_bounds[:-1], q_bounds[1:]))
+    k_tiles = list(zip(k_bounds[:-1], k_bounds[1:]))
+
+    def block(qa, qb, ka, kb):
+        """(P, dS) of query rows qa..qb-1 against keys ka..kb-1."""
+        s = float(scale) * (q[qa:qb] @ k[ka:kb].T)
+        if causal:
+            hidden = np.arange(ka, kb)[None, :] > (np.arange(qa, qb) + query_offset)[:, None]
+            s = np.where(hidden, -np.inf, s)
+        rows_lse = lse[qa:qb]
+        seen = np.isfinite(rows_lse)              # rows with no visible key: P = 0
+        prob = np.zeros_like(s)
+        prob[seen] = np.exp(s[seen] - rows_lse[seen][:, None])
+        dprob = do[qa:qb] @ v[ka:kb].T
+        return prob, prob * (dprob - r[qa:qb, None])
+
+    dk, dv = np.zeros_like(k), np.zeros_like(v)
+    for ka, kb in k_tiles:                        # pass 1: key tiles own dK, dV
+        for qa, qb in q_tiles:
+            prob, dscore = block(qa, qb, ka, kb)
+            dv[ka:kb] += prob.T @ do[qa:qb]
+            dk[ka:kb] += float(scale) * (dscore.T @ q[qa:qb])
+    dq = np.zeros_like(q)
+    for qa, qb in q_tiles:                        # pass 2: query tiles own dQ
+        for ka, kb in k_tiles:
+            _, dscore = block(qa, qb, ka, kb)
+            dq[qa:qb] += float(scale) * (dscore @ k[ka:kb])
     return dq, dk, dv
 
 

@@ -208,24 +208,26 @@ def test_planted_mistake_is_caught(name):
 
 def _online_mutant(q, k, v, scale, causal, bounds, *, rescale_o=True, rescale_l=True,
                    safe=True, query_offset=0):
+    """The per-row recurrence with one step optionally broken: the old o or l
+    not rescaled by exp(m - m'), or no safe reference for still-hidden rows."""
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
-    nq = len(q)
-    m = np.full(nq, -np.inf)
-    l = np.zeros(nq)
-    o = np.zeros((nq, v.shape[1]))
-    for lo, hi in zip(bounds[:-1], bounds[1:]):
-        S = scale * (q @ k[lo:hi].T)
-        if causal:
-            S = np.where(np.arange(lo, hi)[None, :] > (np.arange(nq) + query_offset)[:, None],
-                         -np.inf, S)
-        mn = np.maximum(m, S.max(axis=1))
-        ref = np.where(np.isfinite(mn), mn, 0.0) if safe else mn
-        a = np.exp(m - ref)
-        p = np.exp(S - ref[:, None])
-        l = (a if rescale_l else 1.0) * l + p.sum(axis=1)
-        o = (a[:, None] if rescale_o else 1.0) * o + p @ v[lo:hi]
-        m = mn
-    return o / l[:, None], m + np.log(l)
+    out = np.zeros((len(q), v.shape[1]))
+    lse = np.zeros(len(q))
+    for i in range(len(q)):
+        m, l, o = -math.inf, 0.0, np.zeros(v.shape[1])
+        for first, end in zip(bounds[:-1], bounds[1:]):
+            s = [(-math.inf if causal and j > i + query_offset else scale * float(q[i] @ k[j]))
+                 for j in range(first, end)]
+            m_next = max(m, max(s))
+            ref = m_next if (m_next != -math.inf or not safe) else 0.0
+            keep = math.exp(m - ref) if not (math.isinf(m) and math.isinf(ref)) else math.nan
+            w = np.exp(np.array(s) - ref)
+            l = (keep if rescale_l else 1.0) * l + w.sum()
+            o = (keep if rescale_o else 1.0) * o + w @ v[first:end]
+            m = m_next
+        out[i] = o / l
+        lse[i] = m + math.log(l) if l > 0 else -math.inf
+    return out, lse
 
 
 @pytest.mark.parametrize("kw", [dict(rescale_o=False), dict(rescale_l=False)],

@@ -152,3 +152,76 @@ def test_chunked_rows_equal_the_definition(causal):
     part = attention_dropout_bwd_ref_rows(q, k, v, g, 0.3, causal, 6, 17, 70, qr, kr, chunk=16)
     for a, b in zip(part, (full[0][qr], full[1][kr], full[2][kr])):
         np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+
+
+# ---- expectation over seeds: the keep scale and the all-keys normaliser ----
+#
+# Each probability is kept with probability pi = (256 - t) / 256 (a byte >= t
+# of a uniform byte), so E[keep_j] = pi and, with the normaliser counting every
+# visible key, E[O] = sum_j P_j v_j * keep_scale * pi, which is the plain
+# attention output exactly when keep_scale = 256 / (256 - t).  Over S seeds the
+# seed-mean of O then lies within a CLT bound of plain attention: the per-seed
+# variance of one element is keep_scale^2 pi (1 - pi) sum_j P_j^2 v_j^2 (the
+# mask bytes of different keys are independent draws of the generator).  Two
+# other readings -- no keep scale, or a normaliser over the kept keys only --
+# miss the same bound.
+
+_SEEDS = 4000
+
+
+def _expectation_case(t, causal):
+    rng = np.random.default_rng(40 + t)
+    q, k, v = (rng.standard_normal((5, 3)) for _ in range(3))
+    o, lse = attention_ref(q, k, v, 0.8, causal)
+    p = np.exp(0.8 * q @ k.T - lse[:, None])
+    if causal:
+        p = np.tril(p)
+    pi = (256 - t) / 256.0
+    ks = 256.0 / (256 - t)
+    sigma = np.sqrt(ks * ks * pi * (1 - pi) * (p * p) @ (v * v))      # per-seed std of O
+    return q, k, v, o, lse, p, sigma
+
+
+def _seed_mean(fn, n_seeds=_SEEDS):
+    return sum(fn(seed) for seed in range(1000, 1000 + n_seeds)) / n_seeds
+
+
+@pytest.mark.parametrize("t", [64, 128, 192])
+@pytest.mark.parametrize("causal", [False, True])
+def test_dropout_output_is_unbiased_over_seeds(t, causal):
+    q, k, v, o, lse, p, sigma = _expectation_case(t, causal)
+    lses = []
+
+    def one(seed):
+        od, ld = attention_dropout_ref(q, k, v, 0.8, causal, 3, seed, t)
+        lses.append(ld)
+        return od
+
+    mean = _seed_mean(one)
+    bound = 5.0 * sigma / np.sqrt(_SEEDS) + 1e-12
+    assert np.all(np.abs(mean - o) <= bound), np.max(np.abs(mean - o) / bound)
+    # The log-normaliser counts every visible key: the same for every mask.
+    assert all(np.array_equal(ld, lse) for ld in lses)
+
+
+@pytest.mark.parametrize("t", [64, 128, 192])
+def test_other_dropout_readings_miss_the_expectation(t):
+    """Planted readings on the oracle's own masks: no 1/(1 - t/256) factor, or
+    the normaliser taken over kept keys only (a ratio whose mean is not the
+    plain output); each misses the bound the oracle meets."""
+    q, k, v, o, lse, p, sigma = _expectation_case(t, False)
+    bound = 5.0 * sigma / np.sqrt(_SEEDS) + 1e-12
+    pi = (256 - t) / 256.0
+
+    def unscaled(seed):
+        od, _ = attention_dropout_ref(q, k, v, 0.8, False, 3, seed, t)
+        return od * pi                          # the same masks without the keep scale
+
+    def kept_keys_only(seed):
+        keep = dropout_keep(3, np.arange(5), 5, seed, t)
+        w = p * keep
+        den = w.sum(axis=1, keepdims=True)
+        return np.where(den > 0, w @ v / np.where(den > 0, den, 1.0), 0.0)
+
+    for fn in (unscaled, kept_keys_only):
+        assert np.any(np.abs(_seed_mean(fn) - o) > bound), fn.__name__

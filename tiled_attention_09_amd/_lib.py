@@ -5,6 +5,11 @@ Every step of attention runs in the HIP kernels behind the C ABI declared in
 the outputs with torch (device memory is torch's job here) and passes raw
 pointers and the current HIP stream.  There is no fallback: if the library is
 missing, every call raises.
+
+Every tensor a caller passes -- inputs, outputs, workspaces -- is checked for
+dtype, shape, contiguity and device before the C entry point is called: a
+host tensor or a short buffer given as an output would otherwise be written
+out of bounds by a kernel.
 """
 from __future__ import annotations
 
@@ -17,6 +22,24 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
 
 TA_OK, TA_ERR_INVALID_ARG, TA_ERR_UNSUPPORTED, TA_ERR_MISALIGNED, TA_ERR_HIP = range(5)
+
+_P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+# name: (argument types, result type)
+_SIGNATURES = {
+    "attn_fwd": ([_P] * 5 + [_I] * 4 + [_F, _I, _P], _I),
+    "attn_fwd_ex": ([_P] * 5 + [_I] * 7 + [_F, _I, _P], _I),
+    "attn_bwd": ([_P] * 10 + [_I] * 4 + [_F, _I, _P], _I),
+    "attn_bwd_workspace_size": ([_I] * 3, _Z),
+    "attn_quantize_fp8": ([_P] * 3 + [_I] * 3 + [_P], _I),
+    "attn_fwd_fp8": ([_P] * 7 + [_I] * 4 + [_F, _I, _P], _I),
+    "attn_fwd_dropout": ([_P] * 5 + [_I] * 4 + [_F, _I, ctypes.c_uint64, _I, _P], _I),
+    "attn_fwd_split_workspace_size": ([_I] * 5, _Z),
+    "attn_fwd_split": ([_P] * 5 + [_I] * 7 + [_F, _I, _P, _Z, _P], _I),
+    "attn_bwd_ex": ([_P] * 10 + [_I] * 7 + [_F, _I, _P], _I),
+    "attn_bwd_dropout": ([_P] * 10 + [_I] * 4 + [_F, _I, ctypes.c_uint64, _I, _P], _I),
+    "attn_status_string": ([_I], ctypes.c_char_p),
+}
 
 
 def library_path() -> str:
@@ -31,39 +54,10 @@ def load_library() -> ctypes.CDLL:
         if not os.path.exists(path):
             raise RuntimeError("%s is not built; run __graft_entry__.build() (hipcc, gfx950)" % path)
         lib = ctypes.CDLL(path)
-        lib.attn_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [
-            ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
-        lib.attn_fwd.restype = ctypes.c_int
-        lib.attn_fwd_ex.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 7 + [
-            ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
-        lib.attn_fwd_ex.restype = ctypes.c_int
-        lib.attn_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 4 + [
-            ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
-        lib.attn_bwd.restype = ctypes.c_int
-        lib.attn_bwd_workspace_size.argtypes = [ctypes.c_int] * 3
-        lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
-        lib.attn_quantize_fp8.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + [
-            ctypes.c_void_p]
-        lib.attn_quantize_fp8.restype = ctypes.c_int
-        lib.attn_fwd_fp8.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int] * 4 + [
-            ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
-        lib.attn_fwd_fp8.restype = ctypes.c_int
-        lib.attn_fwd_dropout.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [
-            ctypes.c_float, ctypes.c_int, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p]
-        lib.attn_fwd_dropout.restype = ctypes.c_int
-        lib.attn_fwd_split_workspace_size.argtypes = [ctypes.c_int] * 5
-        lib.attn_fwd_split_workspace_size.restype = ctypes.c_size_t
-        lib.attn_fwd_split.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 7 + [
-            ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
-        lib.attn_fwd_split.restype = ctypes.c_int
-        lib.attn_bwd_ex.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 7 + [
-            ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
-        lib.attn_bwd_ex.restype = ctypes.c_int
-        lib.attn_bwd_dropout.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 4 + [
-            ctypes.c_float, ctypes.c_int, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p]
-        lib.attn_bwd_dropout.restype = ctypes.c_int
-        lib.attn_status_string.argtypes = [ctypes.c_int]
-        lib.attn_status_string.restype = ctypes.c_char_p
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
         _lib = lib
     return _lib
 
@@ -71,6 +65,128 @@ def load_library() -> ctypes.CDLL:
 def attn_status_string(status: int) -> str:
     return load_library().attn_status_string(int(status)).decode()
 
+
+def _check(st: int, name: str) -> None:
+    if st != TA_OK:
+        raise RuntimeError("%s failed: %s (status %d)" % (name, attn_status_string(st), st))
+
+
+# ---------------------------------------------------------------- argument checks
+
+def _dev_input(t, name: str, dtype, dims: int | None = 4):
+    """A caller's input: a contiguous device tensor of ``dtype`` with ``dims``
+    dimensions (any number when None); raises ValueError otherwise."""
+    if not getattr(t, "is_cuda", False):
+        raise ValueError("%s must be a device tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s" % (name, dtype))
+    if dims is not None and t.dim() != dims:
+        raise ValueError("%s must have %d dimensions" % (name, dims))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _same_device(ref, *named):
+    """Every (name, tensor) pair in ``named`` lives on ref's device."""
+    for name, t in named:
+        if t.device != ref.device:
+            raise ValueError("%s must be on %s (got %s)" % (name, ref.device, t.device))
+
+
+def _dev_output(t, name: str, shape, dtype, device):
+    """An output buffer: allocated on ``device`` when ``t`` is None, else checked
+    for shape, dtype, contiguity and device."""
+    import torch
+    shape = tuple(int(x) for x in shape)
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if tuple(t.shape) != shape or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous %s tensor of shape %s" % (name, dtype, list(shape)))
+    if not getattr(t, "is_cuda", False) or t.device != device:
+        raise ValueError("%s must be a device tensor on %s" % (name, device))
+    return t
+
+
+def _dev_workspace(t, name: str, need: int, device):
+    """A byte workspace of at least ``need`` bytes on ``device`` (allocated when None)."""
+    import torch
+    if t is None:
+        return torch.empty(max(int(need), 256), dtype=torch.uint8, device=device)
+    if not getattr(t, "is_cuda", False) or t.device != device or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous device buffer on %s" % (name, device))
+    if t.numel() * t.element_size() < need:
+        raise ValueError("%s must hold at least %d bytes" % (name, need))
+    return t
+
+
+def _stream(stream, device) -> int:
+    """The caller's stream handle, or the current stream of ``device``."""
+    if stream is not None:
+        return int(stream)
+    import torch
+    return int(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _scale(scale, d: int) -> ctypes.c_float:
+    """The caller's scale, or 1/sqrt(d) (the lab's default)."""
+    return ctypes.c_float(float(1.0 / math.sqrt(d) if scale is None else scale))
+
+
+def _fwd_buffers(q, k, v, out, lse):
+    """Checks of the square forward's tensors; returns (B, H, N, d, out, lse)."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev_input(t, name, torch.bfloat16)
+    if q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one shape [B, H, N, d]")
+    _same_device(q, ("k", k), ("v", v))
+    B, H, N, d = (int(x) for x in q.shape)
+    out = _dev_output(out, "out", (B, H, N, d), torch.float32, q.device)
+    lse = _dev_output(lse, "lse", (B, H, N), torch.float32, q.device)
+    return B, H, N, d, out, lse
+
+
+def _ex_buffers(q, k, v, out, lse):
+    """Checks of the general-shape forward's tensors; returns
+    (B, H, Nq, Nk, d, dv, out, lse)."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev_input(t, name, torch.bfloat16)
+    _same_device(q, ("k", k), ("v", v))
+    B, H, Nq, d = (int(x) for x in q.shape)
+    if tuple(k.shape[:2]) != (B, H) or int(k.shape[3]) != d or tuple(v.shape[:3]) != tuple(k.shape[:3]):
+        raise ValueError("k must be [B, H, Nk, d] and v [B, H, Nk, dv]")
+    Nk, dv = int(k.shape[2]), int(v.shape[3])
+    out = _dev_output(out, "out", (B, H, Nq, dv), torch.float32, q.device)
+    lse = _dev_output(lse, "lse", (B, H, Nq), torch.float32, q.device)
+    return B, H, Nq, Nk, d, dv, out, lse
+
+
+def _bwd_buffers(q, k, v, o, lse, do, workspace, grads):
+    """Checks of the square backward's tensors; returns (B, H, N, d, workspace, grads)."""
+    import torch
+    for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16),
+                        ("v", v, torch.bfloat16), ("do", do, torch.bfloat16),
+                        ("o", o, torch.float32)):
+        _dev_input(t, name, dt)
+        if t.shape != q.shape:
+            raise ValueError("%s must have q's shape [B, H, N, d]" % name)
+    _dev_input(lse, "lse", torch.float32, 3)
+    _same_device(q, ("k", k), ("v", v), ("do", do), ("o", o), ("lse", lse))
+    B, H, N, d = (int(x) for x in q.shape)
+    if tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be [B, H, N]")
+    workspace = _dev_workspace(workspace, "workspace", attn_bwd_workspace_size(B, H, N), q.device)
+    grads = (None, None, None) if grads is None else tuple(grads)
+    if len(grads) != 3:
+        raise ValueError("grads must be three tensors (dq, dk, dv)")
+    grads = tuple(_dev_output(t, n, (B, H, N, d), torch.float32, q.device)
+                  for t, n in zip(grads, ("dq", "dk", "dv")))
+    return B, H, N, d, workspace, grads
+
+
+# ---------------------------------------------------------------- forward
 
 def attn_fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, H: int,
                  N: int, d: int, scale: float, causal: int, stream: int = 0) -> int:
@@ -87,57 +203,12 @@ def attn_fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None
     Returns (o float32 [B, H, N, d], lse float32 [B, H, N]); ``out``/``lse`` may
     be given to write into existing buffers.  ``scale`` defaults to 1/sqrt(d).
     """
-    import torch
     lib = load_library()
-    if not (q.is_cuda and k.is_cuda and v.is_cuda):
-        raise ValueError("q, k, v must be device tensors")
-    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
-        raise ValueError("q, k, v must be bfloat16")
-    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
-        raise ValueError("q, k, v must share one shape [B, H, N, d]")
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("q, k, v must be contiguous")
-    B, H, N, d = (int(x) for x in q.shape)
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if out.shape != (B, H, N, d) or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be contiguous float32 [B, H, N, d]")
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [B, H, N]")
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                      B, H, N, d, ctypes.c_float(float(scale)), int(bool(causal)), int(stream))
-    if st != TA_OK:
-        raise RuntimeError("attn_fwd failed: %s (status %d)" % (attn_status_string(st), st))
+    B, H, N, d, out, lse = _fwd_buffers(q, k, v, out, lse)
+    _check(lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                        B, H, N, d, _scale(scale, d), int(bool(causal)), _stream(stream, q.device)),
+           "attn_fwd")
     return out, lse
-
-
-def _fwd_buffers(q, k, v, out, lse):
-    """Checks of the square forward's inputs; returns (B, H, N, d, out, lse)."""
-    import torch
-    if not (q.is_cuda and k.is_cuda and v.is_cuda):
-        raise ValueError("q, k, v must be device tensors")
-    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
-        raise ValueError("q, k, v must be bfloat16")
-    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
-        raise ValueError("q, k, v must share one shape [B, H, N, d]")
-    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
-        raise ValueError("q, k, v must be contiguous")
-    B, H, N, d = (int(x) for x in q.shape)
-    if out is None:
-        out = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if out.shape != (B, H, N, d) or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be contiguous float32 [B, H, N, d]")
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [B, H, N]")
-    return B, H, N, d, out, lse
 
 
 def attn_fwd_dropout_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int,
@@ -157,18 +228,12 @@ def attn_fwd_dropout(q, k, v, seed: int, drop_t: int, scale: float | None = None
     drop_t / 256, 0..255) and the output is scaled by 256 / (256 - drop_t).
     ``lse`` is the undropped log-normaliser.  Returns (o, lse).
     """
-    import torch
+    lib = load_library()
     B, H, N, d, out, lse = _fwd_buffers(q, k, v, out, lse)
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = load_library().attn_fwd_dropout(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
-        ctypes.c_float(float(scale)), int(bool(causal)), int(seed) & ((1 << 64) - 1), int(drop_t),
-        int(stream))
-    if st != TA_OK:
-        raise RuntimeError("attn_fwd_dropout failed: %s (status %d)" % (attn_status_string(st), st))
+    _check(lib.attn_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                lse.data_ptr(), B, H, N, d, _scale(scale, d), int(bool(causal)),
+                                int(seed) & ((1 << 64) - 1), int(drop_t), _stream(stream, q.device)),
+           "attn_fwd_dropout")
     return out, lse
 
 
@@ -189,33 +254,12 @@ def attn_fwd_ex(q, k, v, scale: float | None = None, causal: bool = False, query
     key j visible iff j <= i + query_offset).  Returns (o float32 [B, H, Nq, dv],
     lse float32 [B, H, Nq]); rows that see no key get o = 0 and lse = -inf.
     """
-    import torch
     lib = load_library()
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda or t.dtype != torch.bfloat16 or t.dim() != 4 or not t.is_contiguous():
-            raise ValueError("%s must be a contiguous bfloat16 device tensor [B, H, rows, width]"
-                             % name)
-    B, H, Nq, d = (int(x) for x in q.shape)
-    if tuple(k.shape[:2]) != (B, H) or int(k.shape[3]) != d or tuple(v.shape[:3]) != tuple(k.shape[:3]):
-        raise ValueError("k must be [B, H, Nk, d] and v [B, H, Nk, dv]")
-    Nk, dv = int(k.shape[2]), int(v.shape[3])
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty((B, H, Nq, dv), dtype=torch.float32, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    if out.shape != (B, H, Nq, dv) or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be contiguous float32 [B, H, Nq, dv]")
-    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [B, H, Nq]")
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = lib.attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                         B, H, Nq, Nk, d, dv, int(query_offset), ctypes.c_float(float(scale)),
-                         int(bool(causal)), int(stream))
-    if st != TA_OK:
-        raise RuntimeError("attn_fwd_ex failed: %s (status %d)" % (attn_status_string(st), st))
+    B, H, Nq, Nk, d, dv, out, lse = _ex_buffers(q, k, v, out, lse)
+    _check(lib.attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                           B, H, Nq, Nk, d, dv, int(query_offset), _scale(scale, d),
+                           int(bool(causal)), _stream(stream, q.device)),
+           "attn_fwd_ex")
     return out, lse
 
 
@@ -240,38 +284,20 @@ def attn_fwd_split(q, k, v, scale: float | None = None, causal: bool = False,
     results are combined exactly by their log-normalisers.  ``workspace`` (a
     uint8 device tensor of ``attn_fwd_split_workspace_size`` bytes) is
     allocated here when not given.  Returns (o, lse)."""
-    import torch
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda or t.dtype != torch.bfloat16 or t.dim() != 4 or not t.is_contiguous():
-            raise ValueError("%s must be a contiguous bfloat16 device tensor [B, H, rows, width]"
-                             % name)
-    B, H, Nq, d = (int(x) for x in q.shape)
-    if tuple(k.shape[:2]) != (B, H) or int(k.shape[3]) != d or tuple(v.shape[:3]) != tuple(k.shape[:3]):
-        raise ValueError("k must be [B, H, Nk, d] and v [B, H, Nk, dv]")
-    Nk, dv = int(k.shape[2]), int(v.shape[3])
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty((B, H, Nq, dv), dtype=torch.float32, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    if out.shape != (B, H, Nq, dv) or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be contiguous float32 [B, H, Nq, dv]")
-    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [B, H, Nq]")
+    lib = load_library()
+    B, H, Nq, Nk, d, dv, out, lse = _ex_buffers(q, k, v, out, lse)
     need = attn_fwd_split_workspace_size(B, H, Nq, Nk, dv)
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = load_library().attn_fwd_split(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Nq, Nk, d,
-        dv, int(query_offset), ctypes.c_float(float(scale)), int(bool(causal)), workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), int(stream))
-    if st != TA_OK:
-        raise RuntimeError("attn_fwd_split failed: %s (status %d)" % (attn_status_string(st), st))
+    workspace = _dev_workspace(workspace, "workspace", need, q.device)
+    _check(lib.attn_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              lse.data_ptr(), B, H, Nq, Nk, d, dv, int(query_offset),
+                              _scale(scale, d), int(bool(causal)), workspace.data_ptr(),
+                              workspace.numel() * workspace.element_size(),
+                              _stream(stream, q.device)),
+           "attn_fwd_split")
     return out, lse
 
+
+# ---------------------------------------------------------------- backward
 
 def attn_bwd_workspace_size(B: int, H: int, N: int) -> int:
     """Bytes of device workspace ``attn_bwd`` needs (0 if the sizes are out of range)."""
@@ -287,36 +313,6 @@ def attn_bwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, d
                                    stream)
 
 
-def _bwd_buffers(q, k, v, o, lse, do, workspace, grads):
-    """Checks of the backward's inputs; returns (B, H, N, d, workspace, grads)."""
-    import torch
-    for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16),
-                        ("v", v, torch.bfloat16), ("do", do, torch.bfloat16),
-                        ("o", o, torch.float32)):
-        if not t.is_cuda:
-            raise ValueError("%s must be a device tensor" % name)
-        if t.dtype != dt:
-            raise ValueError("%s must be %s" % (name, dt))
-        if t.dim() != 4 or t.shape != q.shape or not t.is_contiguous():
-            raise ValueError("%s must be contiguous with q's shape [B, H, N, d]" % name)
-    B, H, N, d = (int(x) for x in q.shape)
-    if not lse.is_cuda or lse.dtype != torch.float32 or lse.shape != (B, H, N) \
-            or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 device tensor [B, H, N]")
-    ws_bytes = attn_bwd_workspace_size(B, H, N)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
-    if workspace.numel() * workspace.element_size() < ws_bytes or not workspace.is_cuda:
-        raise ValueError("workspace must be a device buffer of at least %d bytes" % ws_bytes)
-    if grads is None:
-        grads = tuple(torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
-                      for _ in range(3))
-    for t in grads:
-        if t.shape != (B, H, N, d) or t.dtype != torch.float32 or not t.is_contiguous():
-            raise ValueError("grads must be contiguous float32 [B, H, N, d]")
-    return B, H, N, d, workspace, grads
-
-
 def attn_bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False,
              workspace=None, grads=None, stream=None):
     """Gradients of ``attn_fwd`` on the GPU.
@@ -327,20 +323,13 @@ def attn_bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = Fal
     at least ``attn_bwd_workspace_size`` bytes) and ``grads`` (three float32
     tensors) may be given to reuse buffers.
     """
-    import torch
     lib = load_library()
-    B, H, N, d, workspace, grads = _bwd_buffers(q, k, v, o, lse, do, workspace, grads)
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    dq, dk, dv = grads
-    st = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                      do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                      workspace.data_ptr(), B, H, N, d, ctypes.c_float(float(scale)),
-                      int(bool(causal)), int(stream))
-    if st != TA_OK:
-        raise RuntimeError("attn_bwd failed: %s (status %d)" % (attn_status_string(st), st))
+    B, H, N, d, workspace, (dq, dk, dv) = _bwd_buffers(q, k, v, o, lse, do, workspace, grads)
+    _check(lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                        do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                        workspace.data_ptr(), B, H, N, d, _scale(scale, d), int(bool(causal)),
+                        _stream(stream, q.device)),
+           "attn_bwd")
     return dq, dk, dv
 
 
@@ -366,11 +355,10 @@ def attn_bwd_ex(q, k, v, o, lse, do, scale: float | None = None, causal: bool = 
     lib = load_library()
     for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16),
                         ("v", v, torch.bfloat16), ("do", do, torch.bfloat16),
-                        ("o", o, torch.float32), ("lse", lse, torch.float32)):
-        if not t.is_cuda or t.dtype != dt or not t.is_contiguous():
-            raise ValueError("%s must be a contiguous %s device tensor" % (name, dt))
-    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
-        raise ValueError("q, k, v must be [B, H, rows, width]")
+                        ("o", o, torch.float32)):
+        _dev_input(t, name, dt)
+    _dev_input(lse, "lse", torch.float32, 3)
+    _same_device(q, ("k", k), ("v", v), ("do", do), ("o", o), ("lse", lse))
     B, H, Nq, d = (int(x) for x in q.shape)
     Nk, dvw = int(k.shape[2]), int(v.shape[3])
     if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape[:3]) != (B, H, Nk):
@@ -378,28 +366,18 @@ def attn_bwd_ex(q, k, v, o, lse, do, scale: float | None = None, causal: bool = 
     if tuple(do.shape) != (B, H, Nq, dvw) or tuple(o.shape) != (B, H, Nq, dvw) \
             or tuple(lse.shape) != (B, H, Nq):
         raise ValueError("do and o must be [B, H, Nq, dv], lse [B, H, Nq]")
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
-    ws_bytes = attn_bwd_workspace_size(B, H, Nq)
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
-    if workspace.numel() * workspace.element_size() < ws_bytes or not workspace.is_cuda:
-        raise ValueError("workspace must be a device buffer of at least %d bytes" % ws_bytes)
+    workspace = _dev_workspace(workspace, "workspace", attn_bwd_workspace_size(B, H, Nq), q.device)
     shapes = ((B, H, Nq, d), (B, H, Nk, d), (B, H, Nk, dvw))
-    if grads is None:
-        grads = tuple(torch.empty(sh, dtype=torch.float32, device=q.device) for sh in shapes)
-    for t, sh in zip(grads, shapes):
-        if tuple(t.shape) != sh or t.dtype != torch.float32 or not t.is_contiguous():
-            raise ValueError("grads must be contiguous float32 dq %s, dk %s, dv %s" % shapes)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    dq, dk, dv = grads
-    st = lib.attn_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                         do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                         workspace.data_ptr(), B, H, Nq, Nk, d, dvw, int(query_offset),
-                         ctypes.c_float(float(scale)), int(bool(causal)), int(stream))
-    if st != TA_OK:
-        raise RuntimeError("attn_bwd_ex failed: %s (status %d)" % (attn_status_string(st), st))
+    grads = (None, None, None) if grads is None else tuple(grads)
+    if len(grads) != 3:
+        raise ValueError("grads must be three tensors (dq, dk, dv)")
+    dq, dk, dv = (_dev_output(t, n, sh, torch.float32, q.device)
+                  for t, n, sh in zip(grads, ("dq", "dk", "dv"), shapes))
+    _check(lib.attn_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                           workspace.data_ptr(), B, H, Nq, Nk, d, dvw, int(query_offset),
+                           _scale(scale, d), int(bool(causal)), _stream(stream, q.device)),
+           "attn_bwd_ex")
     return dq, dk, dv
 
 
@@ -417,23 +395,18 @@ def attn_bwd_dropout(q, k, v, o, lse, do, seed: int, drop_t: int, scale: float |
                      causal: bool = False, workspace=None, grads=None, stream=None):
     """Gradients of ``attn_fwd_dropout`` (same seed, drop_t, scale, causal): the
     mask is regenerated, never stored.  Arguments and results as ``attn_bwd``."""
-    import torch
     lib = load_library()
-    B, H, N, d, workspace, grads = _bwd_buffers(q, k, v, o, lse, do, workspace, grads)
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    dq, dk, dv = grads
-    st = lib.attn_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                              lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                              dv.data_ptr(), workspace.data_ptr(), B, H, N, d,
-                              ctypes.c_float(float(scale)), int(bool(causal)),
-                              int(seed) & ((1 << 64) - 1), int(drop_t), int(stream))
-    if st != TA_OK:
-        raise RuntimeError("attn_bwd_dropout failed: %s (status %d)" % (attn_status_string(st), st))
+    B, H, N, d, workspace, (dq, dk, dv) = _bwd_buffers(q, k, v, o, lse, do, workspace, grads)
+    _check(lib.attn_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                dv.data_ptr(), workspace.data_ptr(), B, H, N, d, _scale(scale, d),
+                                int(bool(causal)), int(seed) & ((1 << 64) - 1), int(drop_t),
+                                _stream(stream, q.device)),
+           "attn_bwd_dropout")
     return dq, dk, dv
 
+
+# ---------------------------------------------------------------- FP8 scores
 
 def attn_quantize_fp8(x, out=None, descale=None, stream=None):
     """Per-head FP8 (OCP E4M3) codes of a bf16 device tensor [..., rows, d].
@@ -443,25 +416,22 @@ def attn_quantize_fp8(x, out=None, descale=None, stream=None):
     """
     import torch
     lib = load_library()
-    if not x.is_cuda or x.dtype != torch.bfloat16 or x.dim() < 2 or not x.is_contiguous():
-        raise ValueError("x must be a contiguous bfloat16 device tensor [..., rows, d]")
+    _dev_input(x, "x", torch.bfloat16, None)
+    if x.dim() < 2:
+        raise ValueError("x must be [..., rows, d]")
     rows, d = int(x.shape[-2]), int(x.shape[-1])
     heads = x.numel() // max(rows * d, 1)
-    if out is None:
-        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    if descale is None:
-        descale = torch.empty(x.shape[:-2], dtype=torch.float32, device=x.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(x.device).cuda_stream
-    st = lib.attn_quantize_fp8(x.data_ptr(), out.data_ptr(), descale.data_ptr(), heads, rows, d,
-                               int(stream))
-    if st != TA_OK:
-        raise RuntimeError("attn_quantize_fp8 failed: %s (status %d)" % (attn_status_string(st), st))
+    out = _dev_output(out, "out", x.shape, torch.uint8, x.device)
+    descale = _dev_output(descale, "descale", x.shape[:-2], torch.float32, x.device)
+    _check(lib.attn_quantize_fp8(x.data_ptr(), out.data_ptr(), descale.data_ptr(), heads, rows, d,
+                                 _stream(stream, x.device)),
+           "attn_quantize_fp8")
     return out, descale
 
 
 def attn_fwd_fp8_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, qd_ptr, kd_ptr, B, H, N, d, scale,
                      causal, stream=0) -> int:
+    """Call the FP8-score forward's C entry point with raw addresses; returns the status."""
     return load_library().attn_fwd_fp8(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, qd_ptr, kd_ptr, B, H,
                                        N, d, ctypes.c_float(scale), causal, stream)
 
@@ -469,31 +439,25 @@ def attn_fwd_fp8_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, qd_ptr, kd_ptr, B, H, 
 def attn_fwd_fp8(q8, k8, v, q_descale, k_descale, scale: float | None = None, causal=False,
                  out=None, lse=None, stream=None):
     """Attention forward with FP8 scores: q8, k8 uint8 E4M3 codes [B, H, N, d]
-    (from attn_quantize_fp8), v bf16 [B, H, N, d], descales float32 [B, H]."""
+    (from attn_quantize_fp8), v bf16 [B, H, N, d], descales float32 [B, H]
+    (positive and finite, as attn_quantize_fp8 writes them)."""
     import torch
     lib = load_library()
-    if q8.dtype != torch.uint8 or k8.dtype != torch.uint8 or v.dtype != torch.bfloat16:
-        raise ValueError("q8, k8 must be uint8 codes and v bfloat16")
-    if q8.dim() != 4 or q8.shape != k8.shape or q8.shape != v.shape:
+    _dev_input(q8, "q8", torch.uint8)
+    _dev_input(k8, "k8", torch.uint8)
+    _dev_input(v, "v", torch.bfloat16)
+    if q8.shape != k8.shape or q8.shape != v.shape:
         raise ValueError("q8, k8, v must share one shape [B, H, N, d]")
-    for t in (q8, k8, v, q_descale, k_descale):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("inputs must be contiguous device tensors")
     B, H, N, d = (int(x) for x in q8.shape)
-    if tuple(q_descale.shape) != (B, H) or tuple(k_descale.shape) != (B, H) \
-            or q_descale.dtype != torch.float32 or k_descale.dtype != torch.float32:
+    _dev_input(q_descale, "q_descale", torch.float32, 2)
+    _dev_input(k_descale, "k_descale", torch.float32, 2)
+    if tuple(q_descale.shape) != (B, H) or tuple(k_descale.shape) != (B, H):
         raise ValueError("descales must be float32 [B, H]")
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
-    if out is None:
-        out = torch.empty((B, H, N, d), dtype=torch.float32, device=q8.device)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q8.device).cuda_stream
-    st = lib.attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v.data_ptr(), out.data_ptr(),
-                          lse.data_ptr(), q_descale.data_ptr(), k_descale.data_ptr(), B, H, N, d,
-                          ctypes.c_float(float(scale)), int(bool(causal)), int(stream))
-    if st != TA_OK:
-        raise RuntimeError("attn_fwd_fp8 failed: %s (status %d)" % (attn_status_string(st), st))
+    _same_device(q8, ("k8", k8), ("v", v), ("q_descale", q_descale), ("k_descale", k_descale))
+    out = _dev_output(out, "out", (B, H, N, d), torch.float32, q8.device)
+    lse = _dev_output(lse, "lse", (B, H, N), torch.float32, q8.device)
+    _check(lib.attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            lse.data_ptr(), q_descale.data_ptr(), k_descale.data_ptr(), B, H, N, d,
+                            _scale(scale, d), int(bool(causal)), _stream(stream, q8.device)),
+           "attn_fwd_fp8")
     return out, lse

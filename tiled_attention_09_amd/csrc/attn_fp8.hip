@@ -61,7 +61,7 @@ extern "C" int attn_quantize_fp8(const void* x, void* out, float* descale, int h
   if (heads < 1 || rows < 1 || rows > kMaxN) return TA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return TA_ERR_UNSUPPORTED;
   if (!aligned(x, 16) || !aligned(out, 16) || !aligned(descale, 4)) return TA_ERR_MISALIGNED;
-  const int64_t n = (int64_t)rows * d;          // a multiple of kQuantPerThread
+  const int64_t n = (int64_t)rows * d;          // a multiple of 64
   const int64_t chunks = (n + tiledattn::kQuantPerBlock - 1) / tiledattn::kQuantPerBlock;
   if (heads > 65535 || chunks > INT32_MAX) return TA_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -69,8 +69,10 @@ extern "C" int attn_quantize_fp8(const void* x, void* out, float* descale, int h
   const auto* xx = static_cast<const uint16_t*>(x);
   const unsigned hb = (unsigned)((heads + 255) / 256);
   tiledattn::fp8_amax_init_kernel<<<dim3(hb), dim3(256), 0, s>>>(bits, heads);
+  const int64_t amax_chunks = (n + tiledattn::kAmaxPerBlock - 1) / tiledattn::kAmaxPerBlock;
+  tiledattn::fp8_amax_kernel<<<dim3((unsigned)amax_chunks, (unsigned)heads),
+                               dim3(tiledattn::kQuantThreads), 0, s>>>(xx, bits, n);
   const dim3 grid((unsigned)chunks, (unsigned)heads);
-  tiledattn::fp8_amax_kernel<<<grid, dim3(tiledattn::kQuantThreads), 0, s>>>(xx, bits, n);
   tiledattn::fp8_quant_kernel<<<grid, dim3(tiledattn::kQuantThreads), 0, s>>>(
       xx, static_cast<uint8_t*>(out), bits, n);
   tiledattn::fp8_descale_kernel<<<dim3(hb), dim3(256), 0, s>>>(bits, heads);

@@ -28,25 +28,30 @@ __global__ __launch_bounds__(256) void fp8_amax_init_kernel(uint32_t* amax_bits,
   if (h < heads) amax_bits[h] = 0u;
 }
 
-// Grid: (chunks of kQuantPerBlock values, heads).
+// Amax pass: each thread reads kAmaxPerThread bf16 values (eight independent
+// 16-byte loads in flight), so a head of 2^20 values takes 64 blocks and the
+// pass streams at HBM rate; one atomic per block.  Grid: (chunks of
+// kAmaxPerBlock values, heads).  n_per_head is a multiple of 64 (rows x d,
+// d = 64 or 128), so a thread's values are all in range or all past the end.
+constexpr int kAmaxPerThread = 64;
+constexpr int kAmaxPerBlock = kQuantThreads * kAmaxPerThread;
+
 __global__ __launch_bounds__(kQuantThreads) void fp8_amax_kernel(const uint16_t* __restrict__ x,
                                                                  uint32_t* amax_bits,
                                                                  int64_t n_per_head) {
   __shared__ uint32_t part[kQuantThreads / 64];
   const int64_t base = (int64_t)blockIdx.y * n_per_head;
-  const int64_t i0 = (int64_t)blockIdx.x * kQuantPerBlock + (int64_t)threadIdx.x * kQuantPerThread;
+  const int64_t i0 = (int64_t)blockIdx.x * kAmaxPerBlock + (int64_t)threadIdx.x * kAmaxPerThread;
   uint32_t m = 0u;   // |x| as bits: bf16 bits << 16 with the sign cleared
   if (i0 < n_per_head) {
     const u32x4* src = reinterpret_cast<const u32x4*>(x + base + i0);
+    u32x4 w[kAmaxPerThread / 8];
 #pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      const u32x4 w = src[v];
+    for (int v = 0; v < kAmaxPerThread / 8; ++v) w[v] = src[v];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        m = max(m, (w[t] << 16) & 0x7fffffffu);
-        m = max(m, w[t] & 0x7fff0000u);
-      }
-    }
+    for (int v = 0; v < kAmaxPerThread / 8; ++v)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) m = max(m, max((w[v][t] << 16) & 0x7fffffffu, w[v][t] & 0x7fff0000u));
   }
   // Wave maximum, then the block's four waves through LDS, then one atomic.
 #pragma unroll

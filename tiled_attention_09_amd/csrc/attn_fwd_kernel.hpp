@@ -234,8 +234,14 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
   // Online-softmax update from a tile's prepared scores s:
   // m' = max(m, max S), alpha = exp(m - m'), p = exp(S - m'), l' = alpha l + sum p.
   // Returns alpha; p goes to pf as the bf16 B operand of the value product.
+  // In the square instances without dropout the sum is formed in `values`
+  // from the fp32 p kept in pe (the adds then run under the value products,
+  // where the vector unit is otherwise idle); the general-shape and dropout
+  // instances keep it here (the live p would make them spill).
+  constexpr bool kSumInValues = !GENERAL && !DROPOUT;
   // Dropout mask words of the tile whose softmax runs next (dropout_row_words).
   uint32_t mw[2][4];
+  float pe[32];
   auto softmax = [&](f32x16 (&s)[2], bf16x8 (&pf)[4]) __attribute__((always_inline)) {
     // Row maximum: 32 in-lane values (a chain of 3-input maxima), then the
     // other wave half.
@@ -265,18 +271,19 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
       for (int i = 0; i < 16; ++i) {
         const float arg = POS_SCALE ? __builtin_fmaf(s[kb][i], scale_log2, -cref) : s[kb][i] - cref;
         const float p = __builtin_amdgcn_exp2f(arg);
-        psum += p;
+        if constexpr (kSumInValues) pe[kb * 16 + i] = p;
+        else psum += p;
         // Dropout zeroes the weight in the value product only: the
         // normaliser keeps every visible key.
         const float pv = (DROPOUT && !dropout_keep(mw, kb, i, drop.t)) ? 0.f : p;
         pf[kb * 2 + (i >> 3)][i & 7] = (__bf16)pv;
       }
-    l = __builtin_fmaf(l, alpha, psum);
+    if constexpr (!kSumInValues) l = __builtin_fmaf(l, alpha, psum);
     return alpha;
   };
 
-  // o = alpha o, then O^T (dv x 32 queries) += V^T (dv x 64 keys) P^T (64 keys
-  // x 32 queries).  Without dropout the transposed V operands of the first
+  // (l = alpha l + sum p,) o = alpha o, then O^T (dv x 32 queries) += V^T (dv x
+  // 64 keys) P^T (64 keys x 32 queries).  Without dropout the transposed V operands of the first
   // four products are read before the rescale, so that when some row moved
   // its maximum the 16 DV / 32 multiplies per block run under the latency of
   // those reads instead of ahead of them.  With dropout (whose mask generator
@@ -285,6 +292,12 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
   // otherwise idle there).
   auto values = [&](int j, const TA_LDS uint16_t* vt, const bf16x8 (&pf)[4], float alpha)
                     __attribute__((always_inline)) {
+    if constexpr (kSumInValues) {
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) psum += pe[i];
+      l = __builtin_fmaf(l, alpha, psum);
+    }
     constexpr int NPRE = DROPOUT ? 0 : TV::DB;   // operands read before the rescale
     bf16x8 vpre[TV::DB];
 #pragma unroll
@@ -328,23 +341,27 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
   auto step = [&](int j, const TA_LDS uint8_t* k_next, const TA_LDS uint16_t* v_cur,
                   f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) __attribute__((always_inline)) {
     prepare(j, s_cur);
-    // S_{j+1} is computed even when this wave has no tile j+1 (its last tile):
-    // the stage holds in-bounds data and the result is not used.
     // The shared region runs at raised wave priority, so the other wave on
     // this SIMD (in its own value products) does not hold back its issue.
     __builtin_amdgcn_s_setprio(1);
-    scores(k_next, s_next);
-    const float alpha = softmax(s_cur, pf);
-    // Issue order: four K operand reads ahead, then each product followed by
-    // one read and a share of the softmax's vector instructions.
-    sched_reads<4>();
-    sched_rep<(kScoreReads - 4) / (kScoreMfma - 4 > 0 ? kScoreMfma - 4 : kScoreMfma), kValuPerScore,
-              (kScoreMfma - 4 > 0 ? kScoreMfma - 4 : kScoreMfma)>();
-    sched_rep<0, kValuPerScore, (kScoreMfma - 4 > 0 ? 4 : 0)>();
-    // The probabilities must be complete here, inside the region shared with
-    // the score products: without this use the compiler sinks the
-    // exponentials below the rescale branch, out of reach of the interleave.
-    asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(pf[2]), "v"(pf[3]));
+    float alpha;
+    if (j + 1 < n_w) {
+      // S_{j+1} only for a tile this wave visits (its K stage was filled).
+      scores(k_next, s_next);
+      alpha = softmax(s_cur, pf);
+      // Issue order: four K operand reads ahead, then each product followed by
+      // one read and a share of the softmax's vector instructions.
+      sched_reads<4>();
+      sched_rep<(kScoreReads - 4) / (kScoreMfma - 4 > 0 ? kScoreMfma - 4 : kScoreMfma),
+                kValuPerScore, (kScoreMfma - 4 > 0 ? kScoreMfma - 4 : kScoreMfma)>();
+      sched_rep<0, kValuPerScore, (kScoreMfma - 4 > 0 ? 4 : 0)>();
+      // The probabilities must be complete here, inside the region shared with
+      // the score products: without this use the compiler sinks the
+      // exponentials below the rescale branch, out of reach of the interleave.
+      asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(pf[2]), "v"(pf[3]));
+    } else {
+      alpha = softmax(s_cur, pf);   // the wave's last tile: nothing to overlap
+    }
     __builtin_amdgcn_s_setprio(0);
     values(j, v_cur, pf, alpha);
   };
