@@ -162,8 +162,9 @@ size_t attn_fwd_split_workspace_size(int B, int H, int Nq, int Nk, int dv);
  * (the recurrence of page "22. GPU Engineering: Correctness, Throughput, and
  * Attention", sec. 22.5, applied once to whole key ranges).  The split count
  * is chosen from the sizes alone (grids under 256 workgroups are split up to
- * about 256, grids under 1024 in two; >= 4 key tiles of 64 per split), so
- * results are deterministic for given sizes.
+ * about 256; grids under 1024 in two when Nq <= Nk / 64, where the partial
+ * results stay small next to the keys and values read; >= 4 key tiles of 64
+ * per split), so results are deterministic for given sizes.
  *
  *   workspace       : device, 256-byte aligned, >= attn_fwd_split_workspace_size
  *                     bytes (TA_ERR_INVALID_ARG if smaller, TA_ERR_MISALIGNED if

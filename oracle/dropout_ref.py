@@ -15,13 +15,18 @@ definition used here (this library's reading; the pages give none):
   between rounds.  (32-bit words: one block is 16 random bytes for about 80
   32-bit vector operations on the GPU; the 64-bit variant needs emulated
   128-bit products.)
-* Mask: for head n = b*H + h, query row i and key j,
+* Mask: for head n = b*H + h, the query at absolute position i and key j,
       word = Philox(counter = (i, j >> 4, n, 0), key = (seed mod 2^32, seed >> 32))
       byte = bits 8 (j mod 4) .. +7 of word[(j >> 2) mod 4]   (byte j mod 16, little endian)
       keep(i, j) = byte >= t,    drop probability t / 256,  t in 0..255.
 * Output: O = (P * M) V / (1 - t/256) with P the softmax of the scaled, masked
   scores (the normaliser counts every visible key, kept or dropped); LSE is the
   undropped log-normaliser.  t = 0 keeps everything and is plain attention.
+* General shapes (the lab's decoding-style subproblems of sec. 22.7): query row
+  r of a chunk that starts at position ``query_offset`` is the query at
+  absolute position query_offset + r, both for the causal rule and for the
+  mask counter, so a chunk's outputs are the corresponding rows of the whole
+  problem with the same seed.
 * Gradients (the chain rule through the mask): with Pd = P * M / (1 - t/256),
   dV = Pd^T G, dP = (G V^T) * M / (1 - t/256), dS = P * (dP - rowsum(dP * P)),
   dQ = scale dS K, dK = scale dS^T Q; rowsum(dP * P) still equals
@@ -91,32 +96,41 @@ def dropout_keep(n_head: int, rows, nk: int, seed: int, t: int) -> np.ndarray:
     return raw >= t
 
 
-def _probs(q, k, scale, causal, rows):
+def _probs(q, k, scale, causal, rows, query_offset=0):
+    """(P[rows], LSE[rows]); a row that sees no key (no keys at all) gets P = 0
+    and LSE = -inf (the lab's policy)."""
     s = float(scale) * (q[rows] @ k.T)
-    s = np.where(_visible(q.shape[0], k.shape[0], causal, 0, rows), s, -np.inf)
-    m = s.max(axis=1)
-    p = np.exp(s - m[:, None])
+    s = np.where(_visible(q.shape[0], k.shape[0], causal, query_offset, rows), s, -np.inf)
+    m = s.max(axis=1) if k.shape[0] else np.full(len(rows), -np.inf)
+    live = np.isfinite(m)
+    p = np.exp(s - np.where(live, m, 0.0)[:, None])
     l = p.sum(axis=1)
-    return p / l[:, None], m + np.log(l)
+    p[live] /= l[live][:, None]
+    p[~live] = 0.0
+    lse = np.full(len(rows), -np.inf)
+    lse[live] = m[live] + np.log(l[live])
+    return p, lse
 
 
 def attention_dropout_ref(q, k, v, scale: float, causal: bool, n_head: int, seed: int, t: int,
-                          rows=None):
-    """One head: (O [R, dv], LSE [R]) with the dropout mask above, float64."""
+                          rows=None, query_offset: int = 0):
+    """One head: (O [R, dv], LSE [R]) with the dropout mask above, float64.
+    q [Nq, d], k [Nk, d], v [Nk, dv]; query r sits at position query_offset + r."""
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
-    p, lse = _probs(q, k, scale, causal, rows)
-    keep = dropout_keep(n_head, rows, k.shape[0], seed, t)
+    p, lse = _probs(q, k, scale, causal, rows, query_offset)
+    keep = dropout_keep(n_head, rows + query_offset, k.shape[0], seed, t)
     return (p * keep) @ v / (1.0 - t / 256.0), lse
 
 
 def attention_dropout_bwd_ref(q, k, v, do, scale: float, causal: bool, n_head: int, seed: int,
-                              t: int):
-    """One head: (dQ, dK, dV) of sum(G * O) with O from attention_dropout_ref."""
+                              t: int, query_offset: int = 0):
+    """One head: (dQ, dK, dV) of sum(G * O) with O from attention_dropout_ref
+    (same shapes and offset)."""
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
     rows = np.arange(q.shape[0])
-    p, _ = _probs(q, k, scale, causal, rows)
-    mk = dropout_keep(n_head, rows, k.shape[0], seed, t) / (1.0 - t / 256.0)
+    p, _ = _probs(q, k, scale, causal, rows, query_offset)
+    mk = dropout_keep(n_head, rows + query_offset, k.shape[0], seed, t) / (1.0 - t / 256.0)
     dv = (p * mk).T @ do
     dp = (do @ v.T) * mk
     ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))
@@ -125,7 +139,7 @@ def attention_dropout_bwd_ref(q, k, v, do, scale: float, causal: bool, n_head: i
 
 def attention_dropout_bwd_ref_rows(q, k, v, do, scale: float, causal: bool, n_head: int,
                                    seed: int, t: int, query_rows=None, key_rows=None,
-                                   chunk: int = 1024):
+                                   chunk: int = 1024, query_offset: int = 0):
     """One head: attention_dropout_bwd_ref's dQ[query_rows], dK[key_rows] and
     dV[key_rows] (None: all rows), the same formulas evaluated for a chunk of
     query rows at a time so long sequences fit in memory."""
@@ -138,8 +152,8 @@ def attention_dropout_bwd_ref_rows(q, k, v, do, scale: float, causal: bool, n_he
     dv = np.zeros((kr.size, v.shape[1]))
     for c0 in range(0, n, chunk):
         rows = np.arange(c0, min(n, c0 + chunk))
-        p, _ = _probs(q, k, scale, causal, rows)
-        mk = dropout_keep(n_head, rows, k.shape[0], seed, t) / (1.0 - t / 256.0)
+        p, _ = _probs(q, k, scale, causal, rows, query_offset)
+        mk = dropout_keep(n_head, rows + query_offset, k.shape[0], seed, t) / (1.0 - t / 256.0)
         dp = (do[rows] @ v.T) * mk
         ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))
         dv += (p * mk)[:, kr].T @ do[rows]

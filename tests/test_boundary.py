@@ -378,7 +378,9 @@ def test_bwd_square_entry_still_rejects_empty():
 def test_split_plan_sizes():
     ws = ta.attn_fwd_split_workspace_size
     assert ws(2, 8, 16, 32768, 128) > 0              # 16 workgroups: split
-    assert ws(16, 32, 1, 8192, 128) > 0              # 512 workgroups: split in two
+    assert ws(16, 32, 1, 8192, 128) > 0              # 512 workgroups, one query: split in two
+    assert ws(2, 32, 1024, 8192, 128) == 0           # 512 workgroups, Nq > Nk/64: partials too big
+    assert ws(2, 32, 128, 8192, 128) > 0             # 512 workgroups, Nq = Nk/64: split in two
     assert ws(2, 32, 8192, 8192, 128) == 0           # 4096 workgroups: no split
     assert ws(1, 1, 1, 300, 128) == 0                # fewer than 8 key tiles
     assert ws(1, 1, 0, 4096, 128) == 0               # no queries

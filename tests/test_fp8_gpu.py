@@ -1,15 +1,18 @@
 """GPU parity of the FP8 path: the per-head quantiser (bit-exact codes and
-descales against the oracle's float32 recipe) and the FP8-score forward
-(against the float64 oracle evaluated on the oracle's own codes).
+descales against the oracle's float32 recipe), the FP8-score forward (against
+the float64 oracle evaluated on the oracle's own codes) and the precision of
+the FP8 score product itself.
 
 Bars: max |dO| <= 1e-2 and mean |dO| <= 1e-3 (the bf16 forward's), and per
-row |dLSE_i| <= 1e-3 + 2^-14 * max_j |S_ij|.  Both sides see the same
-quantised Q and K (the codes are checked equal first).  The LSE bar is wider
-than the bf16 path's because the FP8 32x32x64 matrix instruction sums its
-products internally at about 21 significant bits (measured: 63 terms of 2^-6
-added to 448^2 lose 0.109; random E4M3 codes: error up to 3.2e-5 of the
-largest result), so a score S carries an error of order 2^-15 |S|, and LSE,
-a smooth maximum of the scores, moves by at most the largest score error.
+row |dLSE_i| <= 1e-3 + 2^-14 * max_j A_ij with A_ij = |scale q_descale
+k_descale| sum_k |q8_ik k8_jk| over the visible keys j.  Both sides see the
+same quantised Q and K (the codes are checked equal first).  The LSE bar
+follows from the product's own precision: the 32x32x64 FP8 matrix instruction
+sums its products at less than float32 precision, and
+test_fp8_score_product_precision pins |dS_ij| <= 2^-14 A_ij on constructed
+codes against the exact sums (measured: 2^-14.5 at worst on random codes over
+the whole E4M3 range, 2^-17 or less on the structured sums); LSE, a smooth maximum of a row's scores, moves
+by at most the largest score error; 1e-3 covers the float32 softmax itself.
 """
 from __future__ import annotations
 
@@ -24,6 +27,7 @@ pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
 O_MAX, O_MEAN, LSE_MAX = 1e-2, 1e-3, 1e-3
+SCORE_TOL = 2.0 ** -14        # |dS_ij| <= SCORE_TOL * A_ij (test_fp8_score_product_precision)
 
 
 def _ta():
@@ -82,10 +86,10 @@ def _fp8_case(q, k, v, scale, causal, rows=None):
             ro, rl = attention_ref(qf[b, h], kf[b, h], vf[b, h], f32_scale(scale), causal, rows=r)
             sel = slice(None) if r is None else r
             ridx = np.arange(q.shape[2]) if r is None else r
-            sc = f32_scale(scale) * (qf[b, h][ridx] @ kf[b, h].T)
+            amag = abs(f32_scale(scale)) * (np.abs(qf[b, h][ridx]) @ np.abs(kf[b, h]).T)
             if causal:
-                sc = np.where(np.arange(sc.shape[1])[None, :] > ridx[:, None], 0.0, sc)
-            bars.append(1e-3 + 2.0 ** -14 * np.abs(sc).max(axis=1))
+                amag = np.where(np.arange(amag.shape[1])[None, :] > ridx[:, None], 0.0, amag)
+            bars.append(1e-3 + SCORE_TOL * amag.max(axis=1))
             errs_o.append(np.abs(o[b, h][sel] - ro).ravel())
             errs_l.append(np.abs(lse[b, h][sel] - rl))
     return np.concatenate(errs_o), np.concatenate(errs_l), np.concatenate(bars)
@@ -121,3 +125,109 @@ def test_fp8_negative_scale_and_descale_folding():
     q[0, 0] *= 16
     k[0, 2] *= 2.0 ** -6
     _check(*_fp8_case(q.contiguous(), k.contiguous(), v, -0.2, True))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_negative_descales(causal):
+    """Caller-supplied descales of either sign: head 0 has a negative Q descale,
+    head 1 a negative K descale, head 2 both (a positive product).  With a
+    positive scale the instance takes the row maximum on raw scores; a negative
+    descale product must be folded in exactly, not give a wrong maximum."""
+    ta = _ta()
+    q, k, v = make_qkv(1, 3, 333, 128, 91, 4.0)
+    print("case fp8 negative descales causal=%d" % causal, flush=True)
+    q8, qd = ta.attn_quantize_fp8(q.to(DEV))
+    k8, kd = ta.attn_quantize_fp8(k.to(DEV))
+    sign_q = torch.tensor([[-1.0, 1.0, -1.0]], device=DEV)
+    sign_k = torch.tensor([[1.0, -1.0, -1.0]], device=DEV)
+    qd_s, kd_s = (qd * sign_q).contiguous(), (kd * sign_k).contiguous()
+    scale = 1 / np.sqrt(128)
+    o, lse = ta.attn_fwd_fp8(q8, k8, v.to(DEV), qd_s, kd_s, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    rq8, rqd = quantize_per_head(_f64(q))
+    rk8, rkd = quantize_per_head(_f64(k))
+    qf = e4m3_decode(rq8) * (rqd * sign_q.cpu().numpy())[..., None, None]
+    kf = e4m3_decode(rk8) * (rkd * sign_k.cpu().numpy())[..., None, None]
+    vf = _f64(v)
+    o, lse = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    errs_o, errs_l, bars = [], [], []
+    for h in range(3):
+        ro, rl = attention_ref(qf[0, h], kf[0, h], vf[0, h], f32_scale(scale), causal)
+        amag = abs(f32_scale(scale)) * (np.abs(qf[0, h]) @ np.abs(kf[0, h]).T)
+        if causal:
+            amag = np.tril(amag)
+        bars.append(1e-3 + SCORE_TOL * amag.max(axis=1))
+        errs_o.append(np.abs(o[0, h] - ro).ravel())
+        errs_l.append(np.abs(lse[0, h] - rl))
+    _check(np.concatenate(errs_o), np.concatenate(errs_l), np.concatenate(bars))
+
+
+# ---- precision of the FP8 score product itself ----------------------------------
+#
+# With one key per head (N = 1), unit descales and scale 1, a row's LSE is its
+# single score S = <q8, k8> (the kernel forms LSE = (m c) ln 2 with m the
+# product's output and c = log2 e in float32: relative rounding below 2^-21).
+# Products of E4M3 values need at most 8 significant bits and a 128-term sum
+# at most 43, so float64 gives the exact S.  Rounding inside the 32x32x64 FP8
+# instruction is bounded relative to the sum of the magnitudes of its terms,
+# A = sum_k |q8_k k8_k| (terms can cancel, so |S| alone is no scale for it).
+
+
+
+def _code_cases():
+    """64 heads of (q codes, k codes), 128 each: structured sums and random codes."""
+    rng = np.random.default_rng(1234)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = e4m3_decode(np.arange(256, dtype=np.uint8))
+    code_of = {float(v): c for c, v in enumerate(vals) if np.isfinite(v) and c < 0x80}
+    cases = []
+    # 448^2 plus 63 products of 2^-3 * 2^-3 = 2^-6 in the same 64-term block.
+    q = np.zeros(128, np.uint8); k = np.zeros(128, np.uint8)
+    q[0] = k[0] = code_of[448.0]
+    q[1:64] = k[1:64] = code_of[0.125]
+    cases.append((q, k))
+    # The same small terms in the second block (accumulated through the first's output).
+    q = np.zeros(128, np.uint8); k = np.zeros(128, np.uint8)
+    q[0] = k[0] = code_of[448.0]
+    q[64:127] = k[64:127] = code_of[0.125]
+    cases.append((q, k))
+    # Exact cancellation: +448^2 and -448^2, and a large cancelling pair with a tail.
+    q = np.zeros(128, np.uint8); k = np.zeros(128, np.uint8)
+    q[0] = q[1] = code_of[448.0]; k[0] = code_of[448.0]; k[1] = code_of[448.0] | 0x80
+    cases.append((q, k))
+    q = np.zeros(128, np.uint8); k = np.zeros(128, np.uint8)
+    q[0] = q[70] = code_of[448.0]; k[0] = code_of[448.0]; k[70] = code_of[448.0] | 0x80
+    q[5:9] = k[5:9] = code_of[1.0]
+    cases.append((q, k))
+    # Every term the same (a long run of equal products).
+    cases.append((np.full(128, code_of[3.0], np.uint8), np.full(128, code_of[5.0], np.uint8)))
+    # Random codes over the whole finite range, and over a narrower exponent band.
+    while len(cases) < 48:
+        cases.append((rng.choice(finite, 128), rng.choice(finite, 128)))
+    band = np.array([c for c in finite if 0.25 <= abs(vals[c]) <= 64.0], dtype=np.uint8)
+    while len(cases) < 64:
+        cases.append((rng.choice(band, 128), rng.choice(band, 128)))
+    return cases
+
+
+def test_fp8_score_product_precision():
+    ta = _ta()
+    cases = _code_cases()
+    H = len(cases)
+    q8 = np.stack([c[0] for c in cases]).reshape(1, H, 1, 128)
+    k8 = np.stack([c[1] for c in cases]).reshape(1, H, 1, 128)
+    print("case fp8 score product precision: %d constructed single-key heads" % H, flush=True)
+    v = torch.ones((1, H, 1, 128), dtype=torch.bfloat16, device=DEV)
+    ones = torch.ones((1, H), dtype=torch.float32, device=DEV)
+    _, lse = ta.attn_fwd_fp8(torch.from_numpy(q8).to(DEV), torch.from_numpy(k8).to(DEV), v, ones,
+                             ones, scale=1.0, causal=False)
+    torch.cuda.synchronize()
+    got = lse.cpu().double().numpy().reshape(H)
+    qv, kv = e4m3_decode(q8.reshape(H, 128)), e4m3_decode(k8.reshape(H, 128))
+    exact = (qv * kv).sum(axis=1)
+    mag = np.abs(qv * kv).sum(axis=1)
+    err = np.abs(got - exact)
+    rel = err / np.maximum(mag, 1e-300)
+    print("  max |dS|/A = %.3e (2^%.1f); structured cases: %s" % (
+        rel.max(), np.log2(max(rel.max(), 1e-300)), ["%.2e" % x for x in rel[:5]]), flush=True)
+    assert np.all(err <= SCORE_TOL * mag + 2.0 ** -21 * np.abs(exact)), rel.max()

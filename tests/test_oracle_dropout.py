@@ -225,3 +225,71 @@ def test_other_dropout_readings_miss_the_expectation(t):
 
     for fn in (unscaled, kept_keys_only):
         assert np.any(np.abs(_seed_mean(fn) - o) > bound), fn.__name__
+
+
+# ---- general shapes (query offset, Nq != Nk, dv != d) ---------------------------
+#
+# Query r of a chunk starting at position `query_offset` is the query at
+# absolute position query_offset + r, for the causal rule and for the mask
+# counter alike, so a chunk is the corresponding rows of the whole problem.
+
+GENERAL_DROP = [  # (nq, nk, d, dv, offset, causal)
+    (1, 40, 4, 3, 39, True),     # one decoding step at the last position
+    (5, 37, 5, 2, 20, True),     # a chunk in the middle
+    (9, 6, 3, 6, 0, True),       # more queries than keys
+    (6, 33, 4, 4, 0, False),     # cross attention, no mask
+]
+
+
+@pytest.mark.parametrize("nq,nk,d,dv,off,causal", GENERAL_DROP)
+def test_general_zero_threshold_is_plain_attention(nq, nk, d, dv, off, causal):
+    rng = np.random.default_rng(nq + nk)
+    q, k = rng.standard_normal((nq, d)), rng.standard_normal((nk, d))
+    v, g = rng.standard_normal((nk, dv)), rng.standard_normal((nq, dv))
+    o, l = attention_dropout_ref(q, k, v, 0.6, causal, 2, 99, 0, query_offset=off)
+    ro, rl = attention_ref(q, k, v, 0.6, causal, query_offset=off)
+    np.testing.assert_allclose(o, ro, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(l, rl, rtol=0, atol=1e-14)
+    for a, b in zip(attention_dropout_bwd_ref(q, k, v, g, 0.6, causal, 2, 99, 0, query_offset=off),
+                    attention_bwd_ref(q, k, v, g, 0.6, causal, query_offset=off)):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("t", [26, 128])
+def test_query_chunk_is_rows_of_the_whole_problem(t):
+    """A chunk of queries at positions 11..17 over all 30 keys (causal) gives the
+    outputs, LSE and dQ rows of the square problem's rows 11..17."""
+    rng = np.random.default_rng(60 + t)
+    q, k, v, g = (rng.standard_normal((30, 4)) for _ in range(4))
+    o, l = attention_dropout_ref(q, k, v, 0.7, True, 5, 1234, t)
+    oc, lc = attention_dropout_ref(q[11:18], k, v, 0.7, True, 5, 1234, t, query_offset=11)
+    np.testing.assert_allclose(oc, o[11:18], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lc, l[11:18], rtol=0, atol=1e-14)
+    dq = attention_dropout_bwd_ref(q, k, v, g, 0.7, True, 5, 1234, t)[0]
+    dqc = attention_dropout_bwd_ref(q[11:18], k, v, g[11:18], 0.7, True, 5, 1234, t,
+                                    query_offset=11)[0]
+    np.testing.assert_allclose(dqc, dq[11:18], rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("nq,nk,d,dv,off,causal", GENERAL_DROP)
+def test_general_gradients_match_finite_differences(nq, nk, d, dv, off, causal):
+    rng = np.random.default_rng(70 + nq)
+    q, k = rng.standard_normal((nq, d)), rng.standard_normal((nk, d))
+    v, g = rng.standard_normal((nk, dv)), rng.standard_normal((nq, dv))
+    args = [q, k, v]
+    grads = attention_dropout_bwd_ref(q, k, v, g, 0.5, causal, 4, 31, 100, query_offset=off)
+    h = 1e-5
+    for which in range(3):
+        e = rng.standard_normal(args[which].shape)
+        ap, am = list(args), list(args)
+        ap[which] = args[which] + h * e
+        am[which] = args[which] - h * e
+        fp = (g * attention_dropout_ref(*ap, 0.5, causal, 4, 31, 100, query_offset=off)[0]).sum()
+        fm = (g * attention_dropout_ref(*am, 0.5, causal, 4, 31, 100, query_offset=off)[0]).sum()
+        assert abs((fp - fm) / (2 * h) - (grads[which] * e).sum()) < 1e-7
+
+
+def test_no_keys_gives_the_lab_policy():
+    q = np.ones((3, 4))
+    o, l = attention_dropout_ref(q, np.zeros((0, 4)), np.zeros((0, 2)), 0.5, False, 0, 1, 26)
+    assert np.array_equal(o, np.zeros((3, 2))) and np.all(l == -np.inf)

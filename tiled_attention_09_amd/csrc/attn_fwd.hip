@@ -121,9 +121,12 @@ int forward(const void* q, const void* k, const void* v, float* o, float* lse, i
 // (>= 4) of key tiles.  Grids below one workgroup per compute unit are split
 // up to kSplitFill workgroups (one per CU streaming a long key range measured
 // best: 16 queries over 32768 keys in 16 heads reached 5.2 TB/s with 256
-// workgroups, 4.5 with 512, 3.6 with 1024, 3.7 with 128); grids below
-// kSplitTwo are split in two (a 1024-query chunk over 8192 keys in 64 heads:
-// 9 % faster).
+// workgroups, 4.5 with 512, 3.6 with 1024, 3.7 with 128).  Grids below
+// kSplitTwo are split in two only when the partial results are small next to
+// the keys and values: two fp32 partial rows of dv values, written and read
+// back, per query cost 16 Nq dv bytes against 2 Nk dv bytes of V, so Nq <= Nk/64
+// keeps them under an eighth (a chunk of 1024 queries over 8192 keys, which
+// moved 2.4x its algorithmic bytes split, runs unsplit).
 constexpr int64_t kSplitFill = 256;
 constexpr int64_t kSplitTwo = 1024;
 
@@ -135,6 +138,7 @@ SplitPlan plan_split(int64_t bh, int Nq, int Nk) {
   const int64_t grid = bh * ((Nq + tiledattn::kBM - 1) / tiledattn::kBM);
   const int n_kt = (Nk + tiledattn::kBN - 1) / tiledattn::kBN;
   if (grid == 0 || grid >= kSplitTwo || n_kt < 8) return {1, n_kt};
+  if (grid >= kSplitFill && (int64_t)Nq * 64 > (int64_t)Nk) return {1, n_kt};
   const int64_t want = grid < kSplitFill ? (kSplitFill + grid - 1) / grid : 2;
   int n = (int)(want < n_kt / 4 ? want : n_kt / 4);
   int tiles = (n_kt + n - 1) / n;

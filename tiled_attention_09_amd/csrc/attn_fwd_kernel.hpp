@@ -145,6 +145,20 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
       qf[ks] = __builtin_bit_cast(bf16x8, load16(qr, (uint32_t)(my_q * D + 16 * ks + 8 * hi) * 2u));
   }
 
+  if constexpr (F8 && POS_SCALE) {
+    // The instance takes the row maximum on raw scores, which is right only
+    // for a positive effective scale.  A negative descale product is folded
+    // into Q instead: negating an E4M3 code flips its sign bit, so with every
+    // Q code negated and the scale's magnitude the scaled scores are unchanged.
+    if (scale_log2 < 0.f) {
+      scale_log2 = -scale_log2;
+#pragma unroll
+      for (int ks = 0; ks < KS8; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf8[ks][e] ^= (int)0x80808080u;
+    }
+  }
+
   // Tile copy offsets: the same for every tile (K and V differ only when D != DV).
   uint32_t src_k[TK::LOADS], src_v[TV::LOADS];
   tile_src_offsets<F8 ? 64 : D>(src_k, wave, lane);
