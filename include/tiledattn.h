@@ -36,7 +36,8 @@ typedef enum {
   TA_ERR_INVALID_ARG = 1, /* a size, offset, flag, pointer or scale is out of range */
   TA_ERR_UNSUPPORTED = 2, /* head dimension other than 64 or 128                  */
   TA_ERR_MISALIGNED = 3,  /* q, k, v or o not 16-byte aligned, lse not 4-byte     */
-  TA_ERR_HIP = 4          /* the HIP runtime reported an error at launch          */
+  TA_ERR_HIP = 4,         /* the HIP runtime reported an error at launch          */
+  TA_ERR_TOO_LARGE = 5    /* sizes exceed attn_bwd_noalloc's fixed device scratch */
 } ta_status;
 
 /*
@@ -294,6 +295,29 @@ int attn_bwd_dropout(const void* q, const void* k, const void* v, const float* o
                      const float* lse, const void* dout, float* dq, float* dk, float* dv,
                      void* workspace, int B, int H, int N, int d, float scale, int causal,
                      uint64_t seed, int drop_t, void* stream);
+
+/*
+ * attn_bwd_noalloc -- attn_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results (bit for bit) as attn_bwd, with
+ * the per-row statistics kept in the library's own device scratch instead of
+ * a caller workspace.  The call allocates nothing, neither does the library.
+ *
+ *   scratch : a fixed 16 MiB array per device, held until the process ends;
+ *             it needs 8 * B * H * (N rounded up to even) bytes, so
+ *             B * H * N <= 2^21 rows (sizes beyond it: TA_ERR_TOO_LARGE,
+ *             before any HIP call).  Nothing in it needs to start at zero.
+ *   Every call on one device shares that device's scratch: calls that may
+ *   overlap on one device (different streams, or threads) race and must be
+ *   serialised by the caller.  The first call on a device (with that device
+ *   current) looks up the scratch address once (hipGetSymbolAddress); a
+ *   failure there gives TA_ERR_HIP.
+ *   q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, stream, the
+ *   other errors, ownership and synchronisation: as for attn_bwd.
+ */
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const float* o,
+                     const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                     int B, int H, int N, int d, float scale, int causal, void* stream);
 
 /* Human-readable text for a ta_status value (static storage; never NULL). */
 const char* attn_status_string(int status);

@@ -41,7 +41,7 @@ def declared_functions():
 
 def test_header_declares_entry_points():
     assert declared_functions() == ["attn_bwd", "attn_bwd_dropout", "attn_bwd_ex",
-                                    "attn_bwd_workspace_size",
+                                    "attn_bwd_noalloc", "attn_bwd_workspace_size",
                                     "attn_fwd",
                                     "attn_fwd_dropout", "attn_fwd_ex", "attn_fwd_fp8",
                                     "attn_fwd_split", "attn_fwd_split_workspace_size",
@@ -59,7 +59,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for st in range(5):
+    for st in range(6):
         assert ta.attn_status_string(st)
     assert ta.attn_status_string(99) == "unknown status"
     assert "head dimension" in ta.attn_status_string(ta.TA_ERR_UNSUPPORTED)
@@ -421,3 +421,32 @@ def test_split_invalid(over):
 def test_split_head_dims_and_alignment():
     assert call_split(d=32) == ta.TA_ERR_UNSUPPORTED
     assert call_split(o=A + 8) == ta.TA_ERR_MISALIGNED
+
+
+# ---- the backward without a workspace (library scratch) ----------------------------
+
+def noalloc(**over):
+    args = dict(q=A, k=A, v=A, o=A, lse=A, do=A, dq=A, dk=A, dv=A, B=1, H=2, N=128, d=128,
+                scale=0.1, causal=1)
+    args.update(over)
+    return ta.attn_bwd_noalloc_raw(*(args[n] for n in ("q", "k", "v", "o", "lse", "do", "dq",
+                                                       "dk", "dv", "B", "H", "N", "d", "scale",
+                                                       "causal")), 0)
+
+
+@host_only
+def test_noalloc_rejects_sizes_beyond_its_scratch():
+    """16 MiB of scratch holds 8 bytes per row of B*H*(N rounded up to even): 2^21 rows."""
+    assert noalloc(B=1, H=1, N=(1 << 21) + 2) == ta.TA_ERR_TOO_LARGE
+    assert noalloc(B=2, H=16, N=65538) == ta.TA_ERR_TOO_LARGE
+    assert noalloc(B=64, H=1, N=32769) == ta.TA_ERR_TOO_LARGE      # rounded up to 32770 rows
+
+
+@host_only
+@pytest.mark.parametrize("over,status", [
+    (dict(q=0), ta.TA_ERR_INVALID_ARG), (dict(dv=0), ta.TA_ERR_INVALID_ARG),
+    (dict(N=0), ta.TA_ERR_INVALID_ARG), (dict(causal=2), ta.TA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), ta.TA_ERR_INVALID_ARG), (dict(d=96), ta.TA_ERR_UNSUPPORTED),
+    (dict(dq=A + 8), ta.TA_ERR_MISALIGNED), (dict(lse=A + 2), ta.TA_ERR_MISALIGNED)])
+def test_noalloc_argument_errors_before_any_hip_call(over, status):
+    assert noalloc(**over) == status

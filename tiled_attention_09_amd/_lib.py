@@ -21,7 +21,8 @@ LIB_NAME = "libtiledattn.so"
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
 
-TA_OK, TA_ERR_INVALID_ARG, TA_ERR_UNSUPPORTED, TA_ERR_MISALIGNED, TA_ERR_HIP = range(5)
+(TA_OK, TA_ERR_INVALID_ARG, TA_ERR_UNSUPPORTED, TA_ERR_MISALIGNED, TA_ERR_HIP,
+ TA_ERR_TOO_LARGE) = range(6)
 
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 
@@ -38,6 +39,7 @@ _SIGNATURES = {
     "attn_fwd_split": ([_P] * 5 + [_I] * 7 + [_F, _I, _P, _Z, _P], _I),
     "attn_bwd_ex": ([_P] * 10 + [_I] * 7 + [_F, _I, _P], _I),
     "attn_bwd_dropout": ([_P] * 10 + [_I] * 4 + [_F, _I, ctypes.c_uint64, _I, _P], _I),
+    "attn_bwd_noalloc": ([_P] * 9 + [_I] * 4 + [_F, _I, _P], _I),
     "attn_status_string": ([_I], ctypes.c_char_p),
 }
 
@@ -177,13 +179,18 @@ def _bwd_buffers(q, k, v, o, lse, do, workspace, grads):
     B, H, N, d = (int(x) for x in q.shape)
     if tuple(lse.shape) != (B, H, N):
         raise ValueError("lse must be [B, H, N]")
-    workspace = _dev_workspace(workspace, "workspace", attn_bwd_workspace_size(B, H, N), q.device)
+    if workspace is not _NO_WORKSPACE:
+        workspace = _dev_workspace(workspace, "workspace", attn_bwd_workspace_size(B, H, N),
+                                   q.device)
     grads = (None, None, None) if grads is None else tuple(grads)
     if len(grads) != 3:
         raise ValueError("grads must be three tensors (dq, dk, dv)")
     grads = tuple(_dev_output(t, n, (B, H, N, d), torch.float32, q.device)
                   for t, n in zip(grads, ("dq", "dk", "dv")))
     return B, H, N, d, workspace, grads
+
+
+_NO_WORKSPACE = object()   # _bwd_buffers: the entry point takes no workspace
 
 
 # ---------------------------------------------------------------- forward
@@ -403,6 +410,31 @@ def attn_bwd_dropout(q, k, v, o, lse, do, seed: int, drop_t: int, scale: float |
                                 int(bool(causal)), int(seed) & ((1 << 64) - 1), int(drop_t),
                                 _stream(stream, q.device)),
            "attn_bwd_dropout")
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int,
+                         do_ptr: int, dq_ptr: int, dk_ptr: int, dv_ptr: int, B: int, H: int,
+                         N: int, d: int, scale: float, causal: int, stream: int = 0) -> int:
+    """Call the no-allocation backward's C entry point with raw addresses; returns the status."""
+    return load_library().attn_bwd_noalloc(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr,
+                                           dk_ptr, dv_ptr, B, H, N, d, ctypes.c_float(scale),
+                                           causal, stream)
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False,
+                     grads=None, stream=None):
+    """``attn_bwd`` without a workspace: the library keeps the row statistics in
+    its own fixed device scratch (16 MiB per device, B*H*N <= 2^21), so a caller
+    that passes ``grads`` allocates nothing.  Calls that may overlap on one
+    device race on that scratch.  Returns (dq, dk, dv)."""
+    lib = load_library()
+    B, H, N, d, _, (dq, dk, dv) = _bwd_buffers(q, k, v, o, lse, do, _NO_WORKSPACE, grads)
+    _check(lib.attn_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                dv.data_ptr(), B, H, N, d, _scale(scale, d), int(bool(causal)),
+                                _stream(stream, q.device)),
+           "attn_bwd_noalloc")
     return dq, dk, dv
 
 

@@ -9,6 +9,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "attn_bwd_kernel.hpp"
 #include "tiledattn.h"
@@ -82,14 +83,11 @@ bool valid_rows(int B, int H, int N, bool allow_empty) {
   return bh * stats_stride(N) <= ((int64_t)1 << 34);
 }
 
-// Shared by attn_bwd and attn_bwd_dropout (square = true: the instances with
-// Nk = Nq, offset 0 and dv = d fixed at compile time) and attn_bwd_ex: every
-// check happens before any HIP call.
-template <bool DROPOUT>
-int backward(const void* q, const void* k, const void* v, const float* o, const float* lse,
-             const void* dout, float* dq, float* dk, float* dv, void* workspace, int B, int H,
-             int Nq, int Nk, int d, int dvw, int offset, float scale, int causal,
-             tiledattn::DropoutArgs dr, void* stream, bool square) {
+// Argument checks of every backward entry point (no HIP call).
+int check_backward(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                   const void* dout, float* dq, float* dk, float* dv, const void* workspace,
+                   int B, int H, int Nq, int Nk, int d, int dvw, int offset, float scale,
+                   int causal, bool square) {
   if (!valid_rows(B, H, Nq, !square) || !valid_rows(B, H, Nk, !square)) return TA_ERR_INVALID_ARG;
   // A pointer may be NULL only where its tensor is empty.
   if ((Nq > 0 && (!q || !o || !lse || !dout || !dq || !workspace)) ||
@@ -103,6 +101,20 @@ int backward(const void* q, const void* k, const void* v, const float* o, const 
       !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
       !aligned(workspace, 16) || !aligned(lse, 4))
     return TA_ERR_MISALIGNED;
+  return TA_OK;
+}
+
+// Shared by attn_bwd and attn_bwd_dropout (square = true: the instances with
+// Nk = Nq, offset 0 and dv = d fixed at compile time), attn_bwd_ex and
+// attn_bwd_noalloc: every check happens before any HIP call.
+template <bool DROPOUT>
+int backward(const void* q, const void* k, const void* v, const float* o, const float* lse,
+             const void* dout, float* dq, float* dk, float* dv, void* workspace, int B, int H,
+             int Nq, int Nk, int d, int dvw, int offset, float scale, int causal,
+             tiledattn::DropoutArgs dr, void* stream, bool square) {
+  const int chk = check_backward(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, Nq, Nk, d,
+                                 dvw, offset, scale, causal, square);
+  if (chk != TA_OK) return chk;
   if (Nq == 0 && Nk == 0) return TA_OK;
 
   const Shape sh{B * H, Nq, Nk, offset};
@@ -140,6 +152,30 @@ tiledattn::DropoutArgs dropout_args(uint64_t seed, int drop_t) {
   return dr;
 }
 
+// The library's own device scratch for attn_bwd_noalloc: the row statistics
+// live here instead of in a caller workspace.  Each device that runs the
+// library holds its own copy for the life of the process.  In host code the
+// name `scratch` is only a stand-in for the symbol; its device address comes
+// from hipGetSymbolAddress, once per device, and only that address is used.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+constexpr int kMaxDevices = 64;
+__device__ __attribute__((aligned(256))) uint8_t scratch[kScratchBytes];
+
+int scratch_address(void** out) {
+  static std::mutex mu;
+  static void* table[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!table[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TA_ERR_HIP;
+    table[dev] = p;
+  }
+  *out = table[dev];
+  return TA_OK;
+}
+
 }  // namespace
 
 extern "C" size_t attn_bwd_workspace_size(int B, int H, int N) {
@@ -171,4 +207,24 @@ extern "C" int attn_bwd_dropout(const void* q, const void* k, const void* v, con
   if (drop_t < 0 || drop_t > 255) return TA_ERR_INVALID_ARG;
   return backward<true>(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, N, N, d, d, 0, scale,
                         causal, dropout_args(seed, drop_t), stream, true);
+}
+
+extern "C" int attn_bwd_noalloc(const void* q, const void* k, const void* v, const float* o,
+                                const float* lse, const void* dout, float* dq, float* dk,
+                                float* dv, int B, int H, int N, int d, float scale, int causal,
+                                void* stream) {
+  // Every argument check before any HIP call; the scratch stands in for the
+  // workspace (a non-NULL, aligned placeholder address for the checks, never
+  // dereferenced).
+  const void* placeholder = reinterpret_cast<const void*>((uintptr_t)256);
+  const int chk = check_backward(q, k, v, o, lse, dout, dq, dk, dv, placeholder, B, H, N, N, d, d,
+                                 0, scale, causal, true);
+  if (chk != TA_OK) return chk;
+  if ((size_t)B * (size_t)H * (size_t)stats_stride(N) * 8u > kScratchBytes)
+    return TA_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  const int st = scratch_address(&ws);
+  if (st != TA_OK) return st;
+  return backward<false>(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, N, N, d, d, 0, scale, causal,
+                         tiledattn::DropoutArgs{}, stream, true);
 }

@@ -254,6 +254,8 @@ extern "C" const char* attn_status_string(int status) {
     case TA_ERR_UNSUPPORTED: return "unsupported head dimension (64 or 128 only)";
     case TA_ERR_MISALIGNED: return "misaligned pointer (q, k, v, o need 16 bytes; lse 4 bytes)";
     case TA_ERR_HIP: return "HIP runtime error at launch";
+    case TA_ERR_TOO_LARGE:
+      return "sizes exceed the fixed device scratch of attn_bwd_noalloc (16 MiB: B*H*N <= 2^21)";
     default: return "unknown status";
   }
 }
