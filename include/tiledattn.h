@@ -144,6 +144,18 @@ int attn_fwd_fp8(const void* q8, const void* k8, const void* v, float* o, float*
                  float scale, int causal, void* stream);
 
 /*
+ * attn_fwd_fp8_ex -- attn_fwd_fp8 for the general shapes of attn_fwd_ex:
+ * q8 [B, H, Nq, 128] and k8 [B, H, Nk, 128] E4M3 codes, v bf16 [B, H, Nk, dv],
+ * o fp32 [B, H, Nq, dv], lse [B, H, Nq]; query r at position query_offset + r.
+ *   d       : 128 only; dv: 64 or 128 (TA_ERR_UNSUPPORTED otherwise).
+ *   q_descale, k_descale, scale: as for attn_fwd_fp8; everything else as for
+ *   attn_fwd_ex (Nq, Nk in 0 .. 2^22; no keys gives O = 0, LSE = -inf).
+ */
+int attn_fwd_fp8_ex(const void* q8, const void* k8, const void* v, float* o, float* lse,
+                    const float* q_descale, const float* k_descale, int B, int H, int Nq, int Nk,
+                    int d, int dv, int query_offset, float scale, int causal, void* stream);
+
+/*
  * attn_fwd_split_workspace_size -- bytes of device workspace attn_fwd_split
  * uses for these sizes (0: no split is planned, and attn_fwd_split is
  * attn_fwd_ex).  Returns 0 also for sizes out of range.
@@ -205,6 +217,20 @@ int attn_fwd_split(const void* q, const void* k, const void* v, float* o, float*
 int attn_fwd_dropout(const void* q, const void* k, const void* v, float* o, float* lse, int B,
                      int H, int N, int d, float scale, int causal, uint64_t seed, int drop_t,
                      void* stream);
+
+/*
+ * attn_fwd_dropout_ex -- attn_fwd_dropout for the general shapes of
+ * attn_fwd_ex (Nq queries at positions query_offset .. query_offset + Nq - 1,
+ * Nk keys, value width dv).  The mask byte of query row r is that of absolute
+ * position i = query_offset + r in the formula of attn_fwd_dropout, so a chunk
+ * of queries gets exactly the rows of the whole problem with the same seed
+ * (the lab's decoding-style subproblems, page "22. GPU Engineering:
+ * Correctness, Throughput, and Attention", sec. 22.7).
+ *   seed, drop_t: as for attn_fwd_dropout; everything else as for attn_fwd_ex.
+ */
+int attn_fwd_dropout_ex(const void* q, const void* k, const void* v, float* o, float* lse,
+                        int B, int H, int Nq, int Nk, int d, int dv, int query_offset,
+                        float scale, int causal, uint64_t seed, int drop_t, void* stream);
 
 /*
  * attn_bwd_workspace_size -- bytes of device workspace attn_bwd needs for
@@ -295,6 +321,18 @@ int attn_bwd_dropout(const void* q, const void* k, const void* v, const float* o
                      const float* lse, const void* dout, float* dq, float* dk, float* dv,
                      void* workspace, int B, int H, int N, int d, float scale, int causal,
                      uint64_t seed, int drop_t, void* stream);
+
+/*
+ * attn_bwd_dropout_ex -- the gradients of attn_fwd_dropout_ex (same shapes,
+ * offset, seed and drop_t; the mask is regenerated from the absolute query
+ * positions).  Arguments, workspace (attn_bwd_workspace_size(B, H, Nq)),
+ * determinism and errors as for attn_bwd_ex.
+ */
+int attn_bwd_dropout_ex(const void* q, const void* k, const void* v, const float* o,
+                        const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                        void* workspace, int B, int H, int Nq, int Nk, int d, int dv_width,
+                        int query_offset, float scale, int causal, uint64_t seed, int drop_t,
+                        void* stream);
 
 /*
  * attn_bwd_noalloc -- attn_bwd for callers that cannot allocate device memory

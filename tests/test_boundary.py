@@ -40,10 +40,12 @@ def declared_functions():
 
 
 def test_header_declares_entry_points():
-    assert declared_functions() == ["attn_bwd", "attn_bwd_dropout", "attn_bwd_ex",
+    assert declared_functions() == ["attn_bwd", "attn_bwd_dropout", "attn_bwd_dropout_ex",
+                                    "attn_bwd_ex",
                                     "attn_bwd_noalloc", "attn_bwd_workspace_size",
                                     "attn_fwd",
-                                    "attn_fwd_dropout", "attn_fwd_ex", "attn_fwd_fp8",
+                                    "attn_fwd_dropout", "attn_fwd_dropout_ex", "attn_fwd_ex",
+                                    "attn_fwd_fp8", "attn_fwd_fp8_ex",
                                     "attn_fwd_split", "attn_fwd_split_workspace_size",
                                     "attn_quantize_fp8", "attn_status_string"]
 
@@ -450,3 +452,34 @@ def test_noalloc_rejects_sizes_beyond_its_scratch():
     (dict(dq=A + 8), ta.TA_ERR_MISALIGNED), (dict(lse=A + 2), ta.TA_ERR_MISALIGNED)])
 def test_noalloc_argument_errors_before_any_hip_call(over, status):
     assert noalloc(**over) == status
+
+
+# ---- general-shape dropout and FP8 entry points ----------------------------------
+
+@host_only
+def test_general_dropout_and_fp8_argument_errors():
+    lib = ta.load_library()
+    sc = ctypes.c_float(0.1)
+    # attn_fwd_dropout_ex: q k v o lse B H Nq Nk d dv off scale causal seed t stream
+    assert lib.attn_fwd_dropout_ex(A, A, A, A, A, 1, 2, 16, 100, 64, 64, 84, sc, 1, 7, 256, 0) \
+        == ta.TA_ERR_INVALID_ARG
+    assert lib.attn_fwd_dropout_ex(A, A, A, A, A, 1, 2, 16, 100, 96, 64, 84, sc, 1, 7, 26, 0) \
+        == ta.TA_ERR_UNSUPPORTED
+    assert lib.attn_fwd_dropout_ex(A, A, A, A, A, 1, 2, 16, 100, 64, 64, -1, sc, 1, 7, 26, 0) \
+        == ta.TA_ERR_INVALID_ARG
+    # attn_bwd_dropout_ex: ... workspace B H Nq Nk d dv off scale causal seed t stream
+    assert lib.attn_bwd_dropout_ex(*([A] * 10), 1, 2, 16, 100, 64, 64, 84, sc, 1, 7, -1, 0) \
+        == ta.TA_ERR_INVALID_ARG
+    assert lib.attn_bwd_dropout_ex(*([A] * 9), 0, 1, 2, 16, 100, 64, 64, 84, sc, 1, 7, 26, 0) \
+        == ta.TA_ERR_INVALID_ARG
+    # attn_fwd_fp8_ex: q8 k8 v o lse qd kd B H Nq Nk d dv off scale causal stream
+    assert lib.attn_fwd_fp8_ex(*([A] * 7), 1, 2, 16, 100, 64, 64, 84, sc, 1, 0) \
+        == ta.TA_ERR_UNSUPPORTED                                   # d = 64
+    assert lib.attn_fwd_fp8_ex(*([A] * 7), 1, 2, 16, 100, 128, 96, 84, sc, 1, 0) \
+        == ta.TA_ERR_UNSUPPORTED                                   # dv = 96
+    assert lib.attn_fwd_fp8_ex(*([A] * 5), 0, A, 1, 2, 16, 100, 128, 64, 84, sc, 1, 0) \
+        == ta.TA_ERR_INVALID_ARG                                   # no q descale
+    assert lib.attn_fwd_fp8_ex(*([A] * 7), 1, 2, 16, 100, 128, 64, 84, sc, 3, 0) \
+        == ta.TA_ERR_INVALID_ARG                                   # causal flag
+    assert lib.attn_fwd_fp8_ex(A + 4, *([A] * 6), 1, 2, 16, 100, 128, 64, 84, sc, 1, 0) \
+        == ta.TA_ERR_MISALIGNED

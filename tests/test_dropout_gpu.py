@@ -202,3 +202,89 @@ def test_dropout_backward_deterministic():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.isfinite(x).all() and torch.equal(x, y)
+
+
+# ---- general shapes: attn_fwd_dropout_ex / attn_bwd_dropout_ex -------------------
+#
+# Query row r of a chunk draws the mask row of its absolute position
+# query_offset + r (the oracle's reading), so a chunk is the corresponding rows
+# of the whole problem.  Same bars as above.
+
+GENERAL_CASES = {  # name: (B, H, Nq, Nk, d, dv, offset, causal)
+    "decode_step": (1, 4, 1, 1000, 128, 128, 999, True),
+    "chunk_100_of_1000": (1, 3, 100, 1000, 64, 64, 900, True),
+    "more_queries_than_keys": (1, 2, 300, 130, 64, 64, 0, True),
+    "dv_smaller": (2, 2, 200, 333, 128, 64, 133, True),
+    "dv_larger": (1, 3, 129, 257, 64, 128, 128, True),
+    "cross_noncausal_ragged": (2, 2, 65, 1003, 128, 128, 0, False),
+}
+
+
+def _general_inputs(B, H, Nq, Nk, d, dv, seed):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn((B, H, Nq, d), generator=g)
+    k = torch.randn((B, H, Nk, d), generator=g)
+    v = torch.randn((B, H, Nk, dv), generator=g)
+    do = torch.randn((B, H, Nq, dv), generator=g)
+    return tuple(x.to(torch.bfloat16).contiguous() for x in (q, k, v, do))
+
+
+@pytest.mark.parametrize("t", [26, 230])
+@pytest.mark.parametrize("name", sorted(GENERAL_CASES))
+def test_dropout_general_forward_and_backward(name, t):
+    B, H, Nq, Nk, d, dv, off, causal = GENERAL_CASES[name]
+    print("case dropout general %s t=%d" % (name, t), flush=True)
+    ta = _ta()
+    scale, seed = 1.0 / np.sqrt(d), 4242 + Nq
+    q, k, v, g = _general_inputs(B, H, Nq, Nk, d, dv, 300 + Nq + Nk)
+    qd, kd, vd, gd = (x.to(DEV) for x in (q, k, v, g))
+    o, lse = ta.attn_fwd_dropout_ex(qd, kd, vd, seed, t, scale=scale, causal=causal,
+                                    query_offset=off)
+    grads = ta.attn_bwd_dropout_ex(qd, kd, vd, o, lse, gd, seed, t, scale=scale, causal=causal,
+                                   query_offset=off)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    got = tuple(x.cpu().double().numpy() for x in grads)
+    eo, el, rq, rk, rv = [], [], [], [], []
+    for b in range(B):
+        for h in range(H):
+            n = b * H + h
+            args = (_f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h]))
+            ro, rl = attention_dropout_ref(*args, f32_scale(scale), causal, n, seed, t,
+                                           query_offset=off)
+            eo.append(np.abs(o[b, h] - ro).ravel())
+            el.append(np.abs(lse[b, h] - rl))
+            ref = attention_dropout_bwd_ref_rows(*args, _f64(g[b, h]), f32_scale(scale), causal, n,
+                                                 seed, t, query_offset=off)
+            rq.append(ref[0]); rk.append(ref[1]); rv.append(ref[2])
+    eo, el = np.concatenate(eo), np.concatenate(el)
+    ks = 256.0 / (256.0 - t)
+    msg = "max|dO| %.3e mean|dO| %.3e max|dLSE| %.3e" % (eo.max(), eo.mean(), el.max())
+    print("  " + msg, flush=True)
+    assert eo.max() <= O_MAX * ks and eo.mean() <= O_MEAN * ks and el.max() <= LSE_MAX, msg
+    ref = tuple(np.stack(x).reshape(B, H, *x[0].shape) for x in (rq, rk, rv))
+    _check_bwd(got, ref, "general dropout backward")
+
+
+def test_dropout_general_zero_threshold_is_attn_fwd_ex():
+    ta = _ta()
+    q, k, v, _ = (x.to(DEV) for x in _general_inputs(1, 3, 100, 1000, 64, 128, 77))
+    a = ta.attn_fwd_ex(q, k, v, causal=True, query_offset=900)
+    b = ta.attn_fwd_dropout_ex(q, k, v, 5, 0, causal=True, query_offset=900)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_dropout_chunk_is_rows_of_the_square_problem():
+    """Queries 640..767 of a square causal problem run as a chunk at offset 640
+    give the same rows as the square dropout forward (same seed, same mask)."""
+    ta = _ta()
+    q, k, v = (x.to(DEV) for x in make_qkv(1, 2, 1000, 128, 78))
+    full = ta.attn_fwd_dropout(q, k, v, 99, 64, causal=True)
+    part = ta.attn_fwd_dropout_ex(q[:, :, 640:768].contiguous(), k, v, 99, 64, causal=True,
+                                  query_offset=640)
+    torch.cuda.synchronize()
+    do = (part[0] - full[0][:, :, 640:768]).abs().max().item()
+    dl = (part[1] - full[1][:, :, 640:768]).abs().max().item()
+    print("  chunk vs square rows: max|dO| %.2e max|dLSE| %.2e" % (do, dl), flush=True)
+    assert do <= 1e-5 and dl <= 1e-6

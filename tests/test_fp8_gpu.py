@@ -231,3 +231,72 @@ def test_fp8_score_product_precision():
     print("  max |dS|/A = %.3e (2^%.1f); structured cases: %s" % (
         rel.max(), np.log2(max(rel.max(), 1e-300)), ["%.2e" % x for x in rel[:5]]), flush=True)
     assert np.all(err <= SCORE_TOL * mag + 2.0 ** -21 * np.abs(exact)), rel.max()
+
+
+# ---- general shapes: attn_fwd_fp8_ex ----------------------------------------------
+
+FP8_GENERAL = {  # name: (B, H, Nq, Nk, dv, offset, causal, mult)
+    "decode_step": (1, 4, 1, 1000, 128, 999, True, 1.0),
+    "chunk_100_of_1000": (1, 3, 100, 1000, 128, 900, True, 4.0),
+    "more_queries_than_keys": (1, 2, 300, 130, 128, 0, True, 1.0),
+    "dv64": (2, 2, 200, 333, 64, 133, True, 1.0),
+    "cross_noncausal_ragged": (2, 2, 65, 1003, 128, 0, False, 1.0),
+    "no_keys": (1, 2, 40, 0, 128, 0, False, 1.0),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FP8_GENERAL))
+def test_fp8_general_shapes(name):
+    B, H, Nq, Nk, dv, off, causal, mult = FP8_GENERAL[name]
+    print("case fp8 general %s" % name, flush=True)
+    ta = _ta()
+    g = torch.Generator().manual_seed(500 + Nq + Nk)
+    q = (torch.randn((B, H, Nq, 128), generator=g) * mult).to(torch.bfloat16).contiguous()
+    k = (torch.randn((B, H, Nk, 128), generator=g) * mult).to(torch.bfloat16).contiguous()
+    v = torch.randn((B, H, Nk, dv), generator=g).to(torch.bfloat16).contiguous()
+    scale = 1 / np.sqrt(128)
+    q8, qd = ta.attn_quantize_fp8(q.to(DEV))
+    if Nk:
+        k8, kd = ta.attn_quantize_fp8(k.to(DEV))
+    else:
+        k8 = torch.empty((B, H, 0, 128), dtype=torch.uint8, device=DEV)
+        kd = torch.ones((B, H), dtype=torch.float32, device=DEV)
+    o, lse = ta.attn_fwd_fp8_ex(q8, k8, v.to(DEV), qd, kd, scale=scale, causal=causal,
+                                query_offset=off)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    if Nk == 0:
+        assert np.array_equal(o, np.zeros_like(o)) and np.all(lse == -np.inf)
+        return
+    rq8, rqd = quantize_per_head(_f64(q))
+    rk8, rkd = quantize_per_head(_f64(k))
+    assert np.array_equal(q8.cpu().numpy(), rq8) and np.array_equal(k8.cpu().numpy(), rk8)
+    qf = e4m3_decode(rq8) * rqd[..., None, None].astype(np.float64)
+    kf = e4m3_decode(rk8) * rkd[..., None, None].astype(np.float64)
+    vf = _f64(v)
+    errs_o, errs_l, bars = [], [], []
+    for b in range(B):
+        for h in range(H):
+            ro, rl = attention_ref(qf[b, h], kf[b, h], vf[b, h], f32_scale(scale), causal,
+                                   query_offset=off)
+            amag = abs(f32_scale(scale)) * (np.abs(qf[b, h]) @ np.abs(kf[b, h]).T)
+            if causal:
+                vis = np.arange(Nk)[None, :] <= (np.arange(Nq) + off)[:, None]
+                amag = np.where(vis, amag, 0.0)
+            bars.append(1e-3 + SCORE_TOL * amag.max(axis=1))
+            errs_o.append(np.abs(o[b, h] - ro).ravel())
+            errs_l.append(np.abs(lse[b, h] - rl))
+    _check(np.concatenate(errs_o), np.concatenate(errs_l), np.concatenate(bars))
+
+
+def test_fp8_ex_square_equals_attn_fwd_fp8():
+    """On a square problem with offset 0 the general instance gives the square
+    instance's results bit for bit."""
+    ta = _ta()
+    q, k, v = make_qkv(2, 2, 333, 128, 95, 4.0)
+    q8, qd = ta.attn_quantize_fp8(q.to(DEV))
+    k8, kd = ta.attn_quantize_fp8(k.to(DEV))
+    a = ta.attn_fwd_fp8(q8, k8, v.to(DEV), qd, kd, causal=True)
+    b = ta.attn_fwd_fp8_ex(q8, k8, v.to(DEV), qd, kd, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])

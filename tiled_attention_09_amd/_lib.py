@@ -40,6 +40,9 @@ _SIGNATURES = {
     "attn_bwd_ex": ([_P] * 10 + [_I] * 7 + [_F, _I, _P], _I),
     "attn_bwd_dropout": ([_P] * 10 + [_I] * 4 + [_F, _I, ctypes.c_uint64, _I, _P], _I),
     "attn_bwd_noalloc": ([_P] * 9 + [_I] * 4 + [_F, _I, _P], _I),
+    "attn_fwd_dropout_ex": ([_P] * 5 + [_I] * 7 + [_F, _I, ctypes.c_uint64, _I, _P], _I),
+    "attn_bwd_dropout_ex": ([_P] * 10 + [_I] * 7 + [_F, _I, ctypes.c_uint64, _I, _P], _I),
+    "attn_fwd_fp8_ex": ([_P] * 7 + [_I] * 7 + [_F, _I, _P], _I),
     "attn_status_string": ([_I], ctypes.c_char_p),
 }
 
@@ -270,6 +273,23 @@ def attn_fwd_ex(q, k, v, scale: float | None = None, causal: bool = False, query
     return out, lse
 
 
+def attn_fwd_dropout_ex(q, k, v, seed: int, drop_t: int, scale: float | None = None,
+                        causal: bool = False, query_offset: int = 0, out=None, lse=None,
+                        stream=None):
+    """``attn_fwd_ex`` with the dropout of ``attn_fwd_dropout``; query row r of
+    the chunk draws the mask row of its absolute position query_offset + r.
+    Returns (o, lse)."""
+    lib = load_library()
+    B, H, Nq, Nk, d, dv, out, lse = _ex_buffers(q, k, v, out, lse)
+    _check(lib.attn_fwd_dropout_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr(), B, H, Nq, Nk, d, dv, int(query_offset),
+                                   _scale(scale, d), int(bool(causal)),
+                                   int(seed) & ((1 << 64) - 1), int(drop_t),
+                                   _stream(stream, q.device)),
+           "attn_fwd_dropout_ex")
+    return out, lse
+
+
 def attn_fwd_split_workspace_size(B: int, H: int, Nq: int, Nk: int, dv: int) -> int:
     """Bytes of device workspace ``attn_fwd_split`` uses (0: it runs unsplit)."""
     return int(load_library().attn_fwd_split_workspace_size(B, H, Nq, Nk, dv))
@@ -350,16 +370,10 @@ def attn_bwd_ex_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int
                                       ctypes.c_float(scale), causal, stream)
 
 
-def attn_bwd_ex(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False,
-                query_offset: int = 0, workspace=None, grads=None, stream=None):
-    """Gradients of ``attn_fwd_ex`` on the GPU (same scale, causal flag, offset).
-
-    q, do: bf16 [B, H, Nq, d] and [B, H, Nq, dv]; k, v: bf16 [B, H, Nk, d],
-    [B, H, Nk, dv]; o float32 [B, H, Nq, dv], lse float32 [B, H, Nq].  Returns
-    (dq [B, H, Nq, d], dk [B, H, Nk, d], dv [B, H, Nk, dv]), float32.
-    """
+def _bwd_ex_buffers(q, k, v, o, lse, do, workspace, grads):
+    """Checks of the general-shape backward's tensors; returns
+    (B, H, Nq, Nk, d, dv, workspace, (dq, dk, dv))."""
     import torch
-    lib = load_library()
     for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16),
                         ("v", v, torch.bfloat16), ("do", do, torch.bfloat16),
                         ("o", o, torch.float32)):
@@ -378,13 +392,45 @@ def attn_bwd_ex(q, k, v, o, lse, do, scale: float | None = None, causal: bool = 
     grads = (None, None, None) if grads is None else tuple(grads)
     if len(grads) != 3:
         raise ValueError("grads must be three tensors (dq, dk, dv)")
-    dq, dk, dv = (_dev_output(t, n, sh, torch.float32, q.device)
+    grads = tuple(_dev_output(t, n, sh, torch.float32, q.device)
                   for t, n, sh in zip(grads, ("dq", "dk", "dv"), shapes))
+    return B, H, Nq, Nk, d, dvw, workspace, grads
+
+
+def attn_bwd_ex(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False,
+                query_offset: int = 0, workspace=None, grads=None, stream=None):
+    """Gradients of ``attn_fwd_ex`` on the GPU (same scale, causal flag, offset).
+
+    q, do: bf16 [B, H, Nq, d] and [B, H, Nq, dv]; k, v: bf16 [B, H, Nk, d],
+    [B, H, Nk, dv]; o float32 [B, H, Nq, dv], lse float32 [B, H, Nq].  Returns
+    (dq [B, H, Nq, d], dk [B, H, Nk, d], dv [B, H, Nk, dv]), float32.
+    """
+    lib = load_library()
+    B, H, Nq, Nk, d, dvw, workspace, (dq, dk, dv) = _bwd_ex_buffers(q, k, v, o, lse, do,
+                                                                    workspace, grads)
     _check(lib.attn_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                            do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                            workspace.data_ptr(), B, H, Nq, Nk, d, dvw, int(query_offset),
                            _scale(scale, d), int(bool(causal)), _stream(stream, q.device)),
            "attn_bwd_ex")
+    return dq, dk, dv
+
+
+def attn_bwd_dropout_ex(q, k, v, o, lse, do, seed: int, drop_t: int, scale: float | None = None,
+                        causal: bool = False, query_offset: int = 0, workspace=None, grads=None,
+                        stream=None):
+    """Gradients of ``attn_fwd_dropout_ex`` (same shapes, offset, seed and drop_t);
+    arguments and results as ``attn_bwd_ex``."""
+    lib = load_library()
+    B, H, Nq, Nk, d, dvw, workspace, (dq, dk, dv) = _bwd_ex_buffers(q, k, v, o, lse, do,
+                                                                    workspace, grads)
+    _check(lib.attn_bwd_dropout_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                   lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                   dv.data_ptr(), workspace.data_ptr(), B, H, Nq, Nk, d, dvw,
+                                   int(query_offset), _scale(scale, d), int(bool(causal)),
+                                   int(seed) & ((1 << 64) - 1), int(drop_t),
+                                   _stream(stream, q.device)),
+           "attn_bwd_dropout_ex")
     return dq, dk, dv
 
 
@@ -492,4 +538,33 @@ def attn_fwd_fp8(q8, k8, v, q_descale, k_descale, scale: float | None = None, ca
                             lse.data_ptr(), q_descale.data_ptr(), k_descale.data_ptr(), B, H, N, d,
                             _scale(scale, d), int(bool(causal)), _stream(stream, q8.device)),
            "attn_fwd_fp8")
+    return out, lse
+
+
+def attn_fwd_fp8_ex(q8, k8, v, q_descale, k_descale, scale: float | None = None, causal=False,
+                    query_offset: int = 0, out=None, lse=None, stream=None):
+    """``attn_fwd_fp8`` for general shapes: q8 [B, H, Nq, 128], k8 [B, H, Nk, 128]
+    E4M3 codes, v bf16 [B, H, Nk, dv], descales float32 [B, H]; query r at
+    position query_offset + r.  Returns (o [B, H, Nq, dv], lse [B, H, Nq])."""
+    import torch
+    lib = load_library()
+    _dev_input(q8, "q8", torch.uint8)
+    _dev_input(k8, "k8", torch.uint8)
+    _dev_input(v, "v", torch.bfloat16)
+    B, H, Nq, d = (int(x) for x in q8.shape)
+    if tuple(k8.shape[:2]) != (B, H) or int(k8.shape[3]) != d or tuple(v.shape[:3]) != tuple(k8.shape[:3]):
+        raise ValueError("k8 must be [B, H, Nk, d] and v [B, H, Nk, dv]")
+    Nk, dv = int(k8.shape[2]), int(v.shape[3])
+    _dev_input(q_descale, "q_descale", torch.float32, 2)
+    _dev_input(k_descale, "k_descale", torch.float32, 2)
+    if tuple(q_descale.shape) != (B, H) or tuple(k_descale.shape) != (B, H):
+        raise ValueError("descales must be float32 [B, H]")
+    _same_device(q8, ("k8", k8), ("v", v), ("q_descale", q_descale), ("k_descale", k_descale))
+    out = _dev_output(out, "out", (B, H, Nq, dv), torch.float32, q8.device)
+    lse = _dev_output(lse, "lse", (B, H, Nq), torch.float32, q8.device)
+    _check(lib.attn_fwd_fp8_ex(q8.data_ptr(), k8.data_ptr(), v.data_ptr(), out.data_ptr(),
+                               lse.data_ptr(), q_descale.data_ptr(), k_descale.data_ptr(), B, H,
+                               Nq, Nk, d, dv, int(query_offset), _scale(scale, d),
+                               int(bool(causal)), _stream(stream, q8.device)),
+           "attn_fwd_fp8_ex")
     return out, lse

@@ -129,18 +129,15 @@ int backward(const void* q, const void* k, const void* v, const float* o, const 
                                                          sh, scale, causal, dr, s)
                    : launch_mask<128, 128, false, DROPOUT>(qq, kk, vv, o, lse, gg, dq, dk, dv, st,
                                                            sh, scale, causal, dr, s);
-  if constexpr (!DROPOUT) {
-    if (d == 64)
-      return dvw == 64 ? launch_mask<64, 64, true, false>(qq, kk, vv, o, lse, gg, dq, dk, dv, st,
+  if (d == 64)
+    return dvw == 64 ? launch_mask<64, 64, true, DROPOUT>(qq, kk, vv, o, lse, gg, dq, dk, dv, st,
                                                           sh, scale, causal, dr, s)
-                       : launch_mask<64, 128, true, false>(qq, kk, vv, o, lse, gg, dq, dk, dv, st,
+                     : launch_mask<64, 128, true, DROPOUT>(qq, kk, vv, o, lse, gg, dq, dk, dv, st,
                                                            sh, scale, causal, dr, s);
-    return dvw == 64 ? launch_mask<128, 64, true, false>(qq, kk, vv, o, lse, gg, dq, dk, dv, st,
+  return dvw == 64 ? launch_mask<128, 64, true, DROPOUT>(qq, kk, vv, o, lse, gg, dq, dk, dv, st,
                                                          sh, scale, causal, dr, s)
-                     : launch_mask<128, 128, true, false>(qq, kk, vv, o, lse, gg, dq, dk, dv, st,
+                   : launch_mask<128, 128, true, DROPOUT>(qq, kk, vv, o, lse, gg, dq, dk, dv, st,
                                                           sh, scale, causal, dr, s);
-  }
-  return TA_ERR_UNSUPPORTED;
 }
 
 tiledattn::DropoutArgs dropout_args(uint64_t seed, int drop_t) {
@@ -197,6 +194,16 @@ extern "C" int attn_bwd_ex(const void* q, const void* k, const void* v, const fl
                            int query_offset, float scale, int causal, void* stream) {
   return backward<false>(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, Nq, Nk, d, dv_width,
                          query_offset, scale, causal, tiledattn::DropoutArgs{}, stream, false);
+}
+
+extern "C" int attn_bwd_dropout_ex(const void* q, const void* k, const void* v, const float* o,
+                                   const float* lse, const void* dout, float* dq, float* dk,
+                                   float* dv, void* workspace, int B, int H, int Nq, int Nk, int d,
+                                   int dv_width, int query_offset, float scale, int causal,
+                                   uint64_t seed, int drop_t, void* stream) {
+  if (drop_t < 0 || drop_t > 255) return TA_ERR_INVALID_ARG;
+  return backward<true>(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, Nq, Nk, d, dv_width,
+                        query_offset, scale, causal, dropout_args(seed, drop_t), stream, false);
 }
 
 extern "C" int attn_bwd_dropout(const void* q, const void* k, const void* v, const float* o,

@@ -172,7 +172,6 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
                           int offset_arg, int stats_stride, int n_kt, float c, float scale,
                           int skip_floor, DropoutArgs drop) {
   static_assert(GENERAL || D == DV, "square instances have one head width");
-  static_assert(!DROPOUT || !GENERAL, "dropout: square shapes");
   const int Nk = GENERAL ? nk_arg : Nq;
   const int offset = GENERAL ? offset_arg : 0;
   using T = Tile<D>;     // Q and K rows, dK
@@ -247,7 +246,7 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     float dd[DROPOUT ? 2 : 1][16];   // dropout: D itself, the dP accumulator starts at 0
     uint32_t mk[2][4];
     if constexpr (DROPOUT)
-      dropout_col_words((uint32_t)qbase, (uint32_t)k0, (uint32_t)bh, drop, lane,
+      dropout_col_words((uint32_t)(qbase + offset), (uint32_t)k0, (uint32_t)bh, drop, lane,
                         (TA_LDS uint32_t*)mk_lds + wave * (32 * 16), mk);
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
@@ -437,7 +436,6 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                         int Nq, int nk_arg, int offset_arg, int stats_stride, int n_qt, float c,
                         float scale, int skip_ceiling, DropoutArgs drop) {
   static_assert(GENERAL || D == DV, "square instances have one head width");
-  static_assert(!DROPOUT || !GENERAL, "dropout: square shapes");
   const int Nk = GENERAL ? nk_arg : Nq;
   const int offset = GENERAL ? offset_arg : 0;
   using T = Tile<D>;     // Q and K rows, dQ
@@ -500,7 +498,8 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     const int key0 = j * kBN;
     const bool edge = (CAUSAL && key0 + kBN - 1 > q0 + offset) || (key0 + kBN > Nk);
     uint32_t mw[2][4];
-    if constexpr (DROPOUT) dropout_row_words((uint32_t)my_q, (uint32_t)j, (uint32_t)bh, drop, hi, mw);
+    if constexpr (DROPOUT)
+      dropout_row_words((uint32_t)(my_q + offset), (uint32_t)j, (uint32_t)bh, drop, hi, mw);
     // One 32-key block at a time: S^T and dP^T (32 keys x 32 queries), then
     // its dS^T, then its share of dQ^T.
 #pragma unroll

@@ -34,18 +34,16 @@ int launch(const void* q, const void* k, const void* v, float* o, float* lse, in
   const uint16_t* vv = static_cast<const uint16_t*>(v);
   // A positive scale lets the row maximum be taken on raw scores (one fused
   // multiply-add per exponent); zero or negative scales take the scaled path.
-  if constexpr (!GENERAL && D == DV) {
-    if (dr) {
-      if (scale_log2 > 0.f)
-        tiledattn::attn_fwd_kernel<D, D, CAUSAL, true, false, false, true>
-            <<<grid, block, 0, stream>>>(qq, kk, vv, o, lse, bh, Nq, Nk, 0, n_qt, scale_log2,
-                                         nullptr, nullptr, *dr, bh, 0);
-      else
-        tiledattn::attn_fwd_kernel<D, D, CAUSAL, false, false, false, true>
-            <<<grid, block, 0, stream>>>(qq, kk, vv, o, lse, bh, Nq, Nk, 0, n_qt, scale_log2,
-                                         nullptr, nullptr, *dr, bh, 0);
-      return hipGetLastError() == hipSuccess ? TA_OK : TA_ERR_HIP;
-    }
+  if (dr) {
+    if (scale_log2 > 0.f)
+      tiledattn::attn_fwd_kernel<D, DV, CAUSAL, true, GENERAL, false, true>
+          <<<grid, block, 0, stream>>>(qq, kk, vv, o, lse, bh, Nq, Nk, offset, n_qt, scale_log2,
+                                       nullptr, nullptr, *dr, bh, 0);
+    else
+      tiledattn::attn_fwd_kernel<D, DV, CAUSAL, false, GENERAL, false, true>
+          <<<grid, block, 0, stream>>>(qq, kk, vv, o, lse, bh, Nq, Nk, offset, n_qt, scale_log2,
+                                       nullptr, nullptr, *dr, bh, 0);
+    return hipGetLastError() == hipSuccess ? TA_OK : TA_ERR_HIP;
   }
   if (scale_log2 > 0.f)
     tiledattn::attn_fwd_kernel<D, DV, CAUSAL, true, GENERAL><<<grid, block, 0, stream>>>(
@@ -86,7 +84,8 @@ int check(const void* q, const void* k, const void* v, float* o, float* lse, int
 }
 
 // Shared by attn_fwd (square = true: the instance with Nk = Nq and offset 0
-// fixed at compile time), attn_fwd_dropout (square, dr set) and attn_fwd_ex.
+// fixed at compile time), attn_fwd_dropout (square, dr set), attn_fwd_ex and
+// attn_fwd_dropout_ex (general, dr set).
 int forward(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H,
             int Nq, int Nk, int d, int dv, int offset, float scale, int causal, void* stream,
             bool square, const tiledattn::DropoutArgs* dr = nullptr) {
@@ -106,13 +105,22 @@ int forward(const void* q, const void* k, const void* v, float* o, float* lse, i
                                               s);
   if (d == 64)
     return dv == 64 ? launch_mask<64, 64, true>(q, k, v, o, lse, ibh, Nq, Nk, offset, scale_log2,
-                                                causal, nullptr, s)
+                                                causal, dr, s)
                     : launch_mask<64, 128, true>(q, k, v, o, lse, ibh, Nq, Nk, offset, scale_log2,
-                                                 causal, nullptr, s);
+                                                 causal, dr, s);
   return dv == 64 ? launch_mask<128, 64, true>(q, k, v, o, lse, ibh, Nq, Nk, offset, scale_log2,
-                                               causal, nullptr, s)
+                                               causal, dr, s)
                   : launch_mask<128, 128, true>(q, k, v, o, lse, ibh, Nq, Nk, offset, scale_log2,
-                                                causal, nullptr, s);
+                                                causal, dr, s);
+}
+
+tiledattn::DropoutArgs dropout_args(uint64_t seed, int drop_t) {
+  tiledattn::DropoutArgs dr;
+  dr.seed_lo = (uint32_t)seed;
+  dr.seed_hi = (uint32_t)(seed >> 32);
+  dr.t = (uint32_t)drop_t;
+  dr.keep_scale = (float)(256.0 / (256.0 - (double)drop_t));
+  return dr;
 }
 
 // Split key ranges (attn_fwd_split): when the (head, query tile) grid is too
@@ -232,12 +240,18 @@ extern "C" int attn_fwd_dropout(const void* q, const void* k, const void* v, flo
                                 int B, int H, int N, int d, float scale, int causal,
                                 uint64_t seed, int drop_t, void* stream) {
   if (N < 1 || drop_t < 0 || drop_t > 255) return TA_ERR_INVALID_ARG;
-  tiledattn::DropoutArgs dr;
-  dr.seed_lo = (uint32_t)seed;
-  dr.seed_hi = (uint32_t)(seed >> 32);
-  dr.t = (uint32_t)drop_t;
-  dr.keep_scale = (float)(256.0 / (256.0 - (double)drop_t));
+  const tiledattn::DropoutArgs dr = dropout_args(seed, drop_t);
   return forward(q, k, v, o, lse, B, H, N, N, d, d, 0, scale, causal, stream, true, &dr);
+}
+
+extern "C" int attn_fwd_dropout_ex(const void* q, const void* k, const void* v, float* o,
+                                   float* lse, int B, int H, int Nq, int Nk, int d, int dv,
+                                   int query_offset, float scale, int causal, uint64_t seed,
+                                   int drop_t, void* stream) {
+  if (drop_t < 0 || drop_t > 255) return TA_ERR_INVALID_ARG;
+  const tiledattn::DropoutArgs dr = dropout_args(seed, drop_t);
+  return forward(q, k, v, o, lse, B, H, Nq, Nk, d, dv, query_offset, scale, causal, stream, false,
+                 &dr);
 }
 
 extern "C" int attn_fwd_ex(const void* q, const void* k, const void* v, float* o, float* lse,

@@ -70,10 +70,11 @@ constexpr int kDropValuPerMfma = 16;
 // GENERAL = false is the square case (Nk = Nq, offset 0) with those facts
 // known at compile time.  F8: Q and K are FP8 (OCP E4M3) codes with per-head
 // descale factors (Q = codes * q_descale[b h], likewise K), the scores use the
-// FP8 matrix product, and the descales fold into the exponent scale (d = 128,
-// square shapes).  DROPOUT: each probability is kept or zeroed by the
-// reproducible mask of `drop` (DropoutArgs) and the output scaled by
-// keep_scale; the normaliser and LSE count every visible key (square shapes).
+// FP8 matrix product, and the descales fold into the exponent scale (d = 128).
+// DROPOUT: each probability is kept or zeroed by the reproducible mask of
+// `drop` (DropoutArgs) and the output scaled by keep_scale; the normaliser and
+// LSE count every visible key; the mask's row counter is the query's absolute
+// position (offset + row), so a query chunk draws the rows of the whole problem.
 // SPLIT: the key range is split over workgroups: bh_count counts (split,
 // head) pairs, workgroup (s, head) covers key tiles [s split_tiles,
 // (s + 1) split_tiles) and writes its own normalised O and LSE at index
@@ -87,8 +88,8 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
                      int n_qt, float scale_log2, const float* __restrict__ q_descale,
                      const float* __restrict__ k_descale, DropoutArgs drop, int heads,
                      int split_tiles) {
-  static_assert(!F8 || (D == 128 && DV == 128 && !GENERAL), "FP8 scores: d = 128, square");
-  static_assert(!DROPOUT || (!GENERAL && !F8), "dropout: square bf16 shapes");
+  static_assert(!F8 || D == 128, "FP8 scores: d = 128");
+  static_assert(!DROPOUT || !F8, "dropout: bf16 scores");
   static_assert(!SPLIT || (GENERAL && !F8 && !DROPOUT), "split key ranges: general bf16 shapes");
   const int Nk = GENERAL ? nk_arg : Nq;
   const int offset = GENERAL ? offset_arg : 0;
@@ -144,7 +145,6 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
     for (int ks = 0; ks < T::KS; ++ks)
       qf[ks] = __builtin_bit_cast(bf16x8, load16(qr, (uint32_t)(my_q * D + 16 * ks + 8 * hi) * 2u));
   }
-
   if constexpr (F8 && POS_SCALE) {
     // The instance takes the row maximum on raw scores, which is right only
     // for a positive effective scale.  A negative descale product is folded
@@ -329,7 +329,7 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             (g == 0 && NPRE) ? vpre[db] : rdv.col_op(vt, g, db), pf[g], oacc[db], 0, 0, 0);
     if constexpr (DROPOUT) {
-      dropout_row_words((uint32_t)my_q, (uint32_t)(j + 1), (uint32_t)bh, drop, hi, mw);
+      dropout_row_words((uint32_t)(my_q + offset), (uint32_t)(j + 1), (uint32_t)bh, drop, hi, mw);
       // Eight transposed V reads in flight, then two more per product.
       sched_mfma_ds_valu<8, 2, 8 * TV::DB, kDropValuPerMfma>(
           std::make_integer_sequence<int, 4 * TV::DB>{});
@@ -402,7 +402,8 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (n_w > kt_lo) scores(k0, sa);
-    if constexpr (DROPOUT) dropout_row_words((uint32_t)my_q, 0u, (uint32_t)bh, drop, hi, mw);
+    if constexpr (DROPOUT)
+      dropout_row_words((uint32_t)(my_q + offset), 0u, (uint32_t)bh, drop, hi, mw);
   }
   for (int j = kt_lo; j < n_kt; j += 2) {
     iter(j, std::integral_constant<int, 0>{});
