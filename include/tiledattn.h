@@ -135,7 +135,7 @@ int attn_quantize_fp8(const void* x, void* out, float* descale, int heads, int r
  *   q8, k8    : device uint8 [B, H, N, d] E4M3 codes (attn_quantize_fp8 output).
  *   v         : device bf16 [B, H, N, d].
  *   q_descale, k_descale : device float32 [B, H].
- *   d         : 128 only (TA_ERR_UNSUPPORTED otherwise).
+ *   d         : 64 or 128 (TA_ERR_UNSUPPORTED otherwise); dv = d.
  *   o, lse, B, H, N, scale, causal, stream, errors: as for attn_fwd
  *   (q8, k8, v, o 16-byte aligned; lse and the descales 4-byte aligned).
  */
@@ -145,9 +145,9 @@ int attn_fwd_fp8(const void* q8, const void* k8, const void* v, float* o, float*
 
 /*
  * attn_fwd_fp8_ex -- attn_fwd_fp8 for the general shapes of attn_fwd_ex:
- * q8 [B, H, Nq, 128] and k8 [B, H, Nk, 128] E4M3 codes, v bf16 [B, H, Nk, dv],
+ * q8 [B, H, Nq, d] and k8 [B, H, Nk, d] E4M3 codes, v bf16 [B, H, Nk, dv],
  * o fp32 [B, H, Nq, dv], lse [B, H, Nq]; query r at position query_offset + r.
- *   d       : 128 only; dv: 64 or 128 (TA_ERR_UNSUPPORTED otherwise).
+ *   d, dv   : 64 or 128 each (TA_ERR_UNSUPPORTED otherwise).
  *   q_descale, k_descale, scale: as for attn_fwd_fp8; everything else as for
  *   attn_fwd_ex (Nq, Nk in 0 .. 2^22; no keys gives O = 0, LSE = -inf).
  */

@@ -252,8 +252,9 @@ def test_fp8_invalid(over):
 
 
 @host_only
-def test_fp8_only_d128():
-    assert call_fp8(d=64) == ta.TA_ERR_UNSUPPORTED
+@pytest.mark.parametrize("d", [32, 96, 256])
+def test_fp8_head_dims(d):
+    assert call_fp8(d=d) == ta.TA_ERR_UNSUPPORTED
 
 
 @host_only
@@ -473,8 +474,8 @@ def test_general_dropout_and_fp8_argument_errors():
     assert lib.attn_bwd_dropout_ex(*([A] * 9), 0, 1, 2, 16, 100, 64, 64, 84, sc, 1, 7, 26, 0) \
         == ta.TA_ERR_INVALID_ARG
     # attn_fwd_fp8_ex: q8 k8 v o lse qd kd B H Nq Nk d dv off scale causal stream
-    assert lib.attn_fwd_fp8_ex(*([A] * 7), 1, 2, 16, 100, 64, 64, 84, sc, 1, 0) \
-        == ta.TA_ERR_UNSUPPORTED                                   # d = 64
+    assert lib.attn_fwd_fp8_ex(*([A] * 7), 1, 2, 16, 100, 96, 64, 84, sc, 1, 0) \
+        == ta.TA_ERR_UNSUPPORTED                                   # d = 96
     assert lib.attn_fwd_fp8_ex(*([A] * 7), 1, 2, 16, 100, 128, 96, 84, sc, 1, 0) \
         == ta.TA_ERR_UNSUPPORTED                                   # dv = 96
     assert lib.attn_fwd_fp8_ex(*([A] * 5), 0, A, 1, 2, 16, 100, 128, 64, 84, sc, 1, 0) \

@@ -1,18 +1,23 @@
 """GPU parity of the FP8 path: the per-head quantiser (bit-exact codes and
 descales against the oracle's float32 recipe), the FP8-score forward (against
 the float64 oracle evaluated on the oracle's own codes) and the precision of
-the FP8 score product itself.
+the FP8 score product itself.  Head dims 64 and 128 (one or two 32x32x64
+products per 32 keys).
 
 Bars: max |dO| <= 1e-2 and mean |dO| <= 1e-3 (the bf16 forward's), and per
-row |dLSE_i| <= 1e-3 + 2^-14 * max_j A_ij with A_ij = |scale q_descale
-k_descale| sum_k |q8_ik k8_jk| over the visible keys j.  Both sides see the
-same quantised Q and K (the codes are checked equal first).  The LSE bar
-follows from the product's own precision: the 32x32x64 FP8 matrix instruction
-sums its products at less than float32 precision, and
-test_fp8_score_product_precision pins |dS_ij| <= 2^-14 A_ij on constructed
-codes against the exact sums (measured: 2^-14.5 at worst on random codes over
-the whole E4M3 range, 2^-17 or less on the structured sums); LSE, a smooth maximum of a row's scores, moves
-by at most the largest score error; 1e-3 covers the float32 softmax itself.
+row |dLSE_i| <= 1e-3 + 2^-11 * max_j G_ij, where G_ij bounds the score
+product's own rounding.  The 32x32x64 FP8 matrix instruction sums its 64
+products at less than float32 precision, with an error that scales with the
+largest product of the block: test_fp8_score_product_precision pins
+|dS_ij| <= 2^-11 sum_b max_{k in b} |q8_ik k8_jk| (b: the 64-term blocks of
+the head dim) on constructed and 1024 random code vectors per head dim
+against the exact sums (measured: 2^-11.6 at worst over 12288 random vectors
+of uniform codes; quantised gaussians stay below 2^-12.6).  In the forward
+tests max_{k in b} |q_ik k_jk| is bounded by max_{k in b} |q_ik| times
+max_{k in b} |k_jk| (descales and scale included), which gives G.  LSE, a
+smooth maximum of a row's scores, moves by at most the largest score error;
+1e-3 covers the float32 softmax itself.  Both sides see the same quantised Q
+and K (the codes are checked equal first).
 """
 from __future__ import annotations
 
@@ -27,7 +32,7 @@ pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
 O_MAX, O_MEAN, LSE_MAX = 1e-2, 1e-3, 1e-3
-SCORE_TOL = 2.0 ** -14        # |dS_ij| <= SCORE_TOL * A_ij (test_fp8_score_product_precision)
+SCORE_TOL = 2.0 ** -11   # |dS_ij| <= SCORE_TOL * sum_b max_{k in b} |q_ik k_jk| (pinned below)
 
 
 def _ta():
@@ -38,6 +43,20 @@ def _ta():
 
 def _f64(t):
     return bf16_bits_to_f64(bf16_bits(t))
+
+
+def _lse_bar(qf, kf, scale, visible=None):
+    """Per-row LSE bar 1e-3 + SCORE_TOL * max_j G_ij for float64 Q [n, d] and
+    K [m, d] (descales applied), G_ij = |scale| sum_b max_{k in b} |q_ik|
+    max_{k in b} |k_jk| over the 64-wide blocks b; visible: [n, m] bool or None."""
+    d = qf.shape[1]
+    g = np.zeros((qf.shape[0], kf.shape[0]))
+    for b in range(0, d, 64):
+        g += np.outer(np.abs(qf[:, b:b + 64]).max(axis=1), np.abs(kf[:, b:b + 64]).max(axis=1))
+    g *= abs(f32_scale(scale))
+    if visible is not None:
+        g = np.where(visible, g, 0.0)
+    return 1e-3 + SCORE_TOL * g.max(axis=1)
 
 
 @pytest.mark.parametrize("case", ["normal", "x4", "tiny", "zero_head", "d64", "ragged"])
@@ -86,10 +105,8 @@ def _fp8_case(q, k, v, scale, causal, rows=None):
             ro, rl = attention_ref(qf[b, h], kf[b, h], vf[b, h], f32_scale(scale), causal, rows=r)
             sel = slice(None) if r is None else r
             ridx = np.arange(q.shape[2]) if r is None else r
-            amag = abs(f32_scale(scale)) * (np.abs(qf[b, h][ridx]) @ np.abs(kf[b, h]).T)
-            if causal:
-                amag = np.where(np.arange(amag.shape[1])[None, :] > ridx[:, None], 0.0, amag)
-            bars.append(1e-3 + SCORE_TOL * amag.max(axis=1))
+            vis = (np.arange(kf.shape[2])[None, :] <= ridx[:, None]) if causal else None
+            bars.append(_lse_bar(qf[b, h][ridx], kf[b, h], scale, vis))
             errs_o.append(np.abs(o[b, h][sel] - ro).ravel())
             errs_l.append(np.abs(lse[b, h][sel] - rl))
     return np.concatenate(errs_o), np.concatenate(errs_l), np.concatenate(bars)
@@ -110,6 +127,15 @@ def test_fp8_forward_full_rows(N, mult, causal):
     _check(*_fp8_case(q, k, v, 1 / np.sqrt(128), causal))
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,mult", [(1, 1.0), (65, 1.0), (1003, 4.0), (2100, 1.0)])
+def test_fp8_forward_d64(N, mult, causal):
+    """d = 64: rows of 64 codes, one 32x32x64 product per 32 keys."""
+    print("case fp8 fwd d=64 N=%d mult=%g causal=%d" % (N, mult, causal), flush=True)
+    q, k, v = make_qkv(2, 3, N, 64, 170 + N, mult)
+    _check(*_fp8_case(q, k, v, 1 / np.sqrt(64), causal))
+
+
 def test_fp8_forward_headline_sampled():
     """B=2, H=32, N=8192, d=128 causal, Q,K x4: 128 sampled rows of every head."""
     w = WORKLOADS["headline"]
@@ -127,21 +153,22 @@ def test_fp8_negative_scale_and_descale_folding():
     _check(*_fp8_case(q.contiguous(), k.contiguous(), v, -0.2, True))
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_fp8_negative_descales(causal):
+def test_fp8_negative_descales(causal, d):
     """Caller-supplied descales of either sign: head 0 has a negative Q descale,
     head 1 a negative K descale, head 2 both (a positive product).  With a
     positive scale the instance takes the row maximum on raw scores; a negative
     descale product must be folded in exactly, not give a wrong maximum."""
     ta = _ta()
-    q, k, v = make_qkv(1, 3, 333, 128, 91, 4.0)
-    print("case fp8 negative descales causal=%d" % causal, flush=True)
+    q, k, v = make_qkv(1, 3, 333, d, 91, 4.0)
+    print("case fp8 negative descales causal=%d d=%d" % (causal, d), flush=True)
     q8, qd = ta.attn_quantize_fp8(q.to(DEV))
     k8, kd = ta.attn_quantize_fp8(k.to(DEV))
     sign_q = torch.tensor([[-1.0, 1.0, -1.0]], device=DEV)
     sign_k = torch.tensor([[1.0, -1.0, -1.0]], device=DEV)
     qd_s, kd_s = (qd * sign_q).contiguous(), (kd * sign_k).contiguous()
-    scale = 1 / np.sqrt(128)
+    scale = 1 / np.sqrt(d)
     o, lse = ta.attn_fwd_fp8(q8, k8, v.to(DEV), qd_s, kd_s, scale=scale, causal=causal)
     torch.cuda.synchronize()
     rq8, rqd = quantize_per_head(_f64(q))
@@ -153,10 +180,9 @@ def test_fp8_negative_descales(causal):
     errs_o, errs_l, bars = [], [], []
     for h in range(3):
         ro, rl = attention_ref(qf[0, h], kf[0, h], vf[0, h], f32_scale(scale), causal)
-        amag = abs(f32_scale(scale)) * (np.abs(qf[0, h]) @ np.abs(kf[0, h]).T)
-        if causal:
-            amag = np.tril(amag)
-        bars.append(1e-3 + SCORE_TOL * amag.max(axis=1))
+        n = qf.shape[2]
+        vis = np.tril(np.ones((n, n), dtype=bool)) if causal else None
+        bars.append(_lse_bar(qf[0, h], kf[0, h], scale, vis))
         errs_o.append(np.abs(o[0, h] - ro).ravel())
         errs_l.append(np.abs(lse[0, h] - rl))
     _check(np.concatenate(errs_o), np.concatenate(errs_l), np.concatenate(bars))
@@ -168,14 +194,16 @@ def test_fp8_negative_descales(causal):
 # single score S = <q8, k8> (the kernel forms LSE = (m c) ln 2 with m the
 # product's output and c = log2 e in float32: relative rounding below 2^-21).
 # Products of E4M3 values need at most 8 significant bits and a 128-term sum
-# at most 43, so float64 gives the exact S.  Rounding inside the 32x32x64 FP8
-# instruction is bounded relative to the sum of the magnitudes of its terms,
-# A = sum_k |q8_k k8_k| (terms can cancel, so |S| alone is no scale for it).
+# at most 43, so float64 gives the exact S.  The rounding inside the 32x32x64
+# FP8 instruction is bounded relative to the largest product of its 64-term
+# block (terms can cancel, so |S| is no scale for it), and the blocks of a
+# d = 128 row add their errors through the float32 accumulator.
 
 
-
-def _code_cases():
-    """64 heads of (q codes, k codes), 128 each: structured sums and random codes."""
+def _code_cases(n_random=1024):
+    """Code vector pairs (128 codes each; d = 64 uses the first 64): structured
+    sums, then random codes over the whole finite E4M3 range and over a
+    narrower exponent band (half each)."""
     rng = np.random.default_rng(1234)
     finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
     vals = e4m3_decode(np.arange(256, dtype=np.uint8))
@@ -201,65 +229,71 @@ def _code_cases():
     cases.append((q, k))
     # Every term the same (a long run of equal products).
     cases.append((np.full(128, code_of[3.0], np.uint8), np.full(128, code_of[5.0], np.uint8)))
-    # Random codes over the whole finite range, and over a narrower exponent band.
-    while len(cases) < 48:
+    n_struct = len(cases)
+    while len(cases) < n_struct + n_random // 2:
         cases.append((rng.choice(finite, 128), rng.choice(finite, 128)))
     band = np.array([c for c in finite if 0.25 <= abs(vals[c]) <= 64.0], dtype=np.uint8)
-    while len(cases) < 64:
+    while len(cases) < n_struct + n_random:
         cases.append((rng.choice(band, 128), rng.choice(band, 128)))
     return cases
 
 
-def test_fp8_score_product_precision():
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_score_product_precision(d):
     ta = _ta()
     cases = _code_cases()
     H = len(cases)
-    q8 = np.stack([c[0] for c in cases]).reshape(1, H, 1, 128)
-    k8 = np.stack([c[1] for c in cases]).reshape(1, H, 1, 128)
-    print("case fp8 score product precision: %d constructed single-key heads" % H, flush=True)
-    v = torch.ones((1, H, 1, 128), dtype=torch.bfloat16, device=DEV)
+    q8 = np.stack([c[0][:d] for c in cases]).reshape(1, H, 1, d)
+    k8 = np.stack([c[1][:d] for c in cases]).reshape(1, H, 1, d)
+    print("case fp8 score product precision d=%d: %d constructed single-key heads" % (d, H),
+          flush=True)
+    v = torch.ones((1, H, 1, d), dtype=torch.bfloat16, device=DEV)
     ones = torch.ones((1, H), dtype=torch.float32, device=DEV)
     _, lse = ta.attn_fwd_fp8(torch.from_numpy(q8).to(DEV), torch.from_numpy(k8).to(DEV), v, ones,
                              ones, scale=1.0, causal=False)
     torch.cuda.synchronize()
     got = lse.cpu().double().numpy().reshape(H)
-    qv, kv = e4m3_decode(q8.reshape(H, 128)), e4m3_decode(k8.reshape(H, 128))
-    exact = (qv * kv).sum(axis=1)
-    mag = np.abs(qv * kv).sum(axis=1)
+    terms = e4m3_decode(q8.reshape(H, d)) * e4m3_decode(k8.reshape(H, d))
+    exact = terms.sum(axis=1)
+    gmax = sum(np.abs(terms[:, b:b + 64]).max(axis=1) for b in range(0, d, 64))
     err = np.abs(got - exact)
-    rel = err / np.maximum(mag, 1e-300)
-    print("  max |dS|/A = %.3e (2^%.1f); structured cases: %s" % (
+    rel = err / np.maximum(gmax, 1e-300)
+    print("  max |dS| / sum of block maxima = %.3e (2^%.1f); structured cases: %s" % (
         rel.max(), np.log2(max(rel.max(), 1e-300)), ["%.2e" % x for x in rel[:5]]), flush=True)
-    assert np.all(err <= SCORE_TOL * mag + 2.0 ** -21 * np.abs(exact)), rel.max()
+    assert np.all(err <= SCORE_TOL * gmax + 2.0 ** -21 * np.abs(exact)), rel.max()
 
 
 # ---- general shapes: attn_fwd_fp8_ex ----------------------------------------------
 
-FP8_GENERAL = {  # name: (B, H, Nq, Nk, dv, offset, causal, mult)
-    "decode_step": (1, 4, 1, 1000, 128, 999, True, 1.0),
-    "chunk_100_of_1000": (1, 3, 100, 1000, 128, 900, True, 4.0),
-    "more_queries_than_keys": (1, 2, 300, 130, 128, 0, True, 1.0),
-    "dv64": (2, 2, 200, 333, 64, 133, True, 1.0),
-    "cross_noncausal_ragged": (2, 2, 65, 1003, 128, 0, False, 1.0),
-    "no_keys": (1, 2, 40, 0, 128, 0, False, 1.0),
+FP8_GENERAL = {  # name: (B, H, Nq, Nk, d, dv, offset, causal, mult)
+    "decode_step": (1, 4, 1, 1000, 128, 128, 999, True, 1.0),
+    "chunk_100_of_1000": (1, 3, 100, 1000, 128, 128, 900, True, 4.0),
+    "more_queries_than_keys": (1, 2, 300, 130, 128, 128, 0, True, 1.0),
+    "dv64": (2, 2, 200, 333, 128, 64, 133, True, 1.0),
+    "cross_noncausal_ragged": (2, 2, 65, 1003, 128, 128, 0, False, 1.0),
+    "no_keys": (1, 2, 40, 0, 128, 128, 0, False, 1.0),
+    "d64_decode_step": (2, 3, 1, 777, 64, 64, 776, True, 1.0),
+    "d64_chunk": (1, 3, 150, 1000, 64, 64, 850, True, 4.0),
+    "d64_dv128_cross": (2, 2, 70, 403, 64, 128, 0, False, 1.0),
+    "d64_dv128_causal": (1, 2, 257, 300, 64, 128, 43, True, 1.0),
 }
 
 
 @pytest.mark.parametrize("name", sorted(FP8_GENERAL))
 def test_fp8_general_shapes(name):
-    B, H, Nq, Nk, dv, off, causal, mult = FP8_GENERAL[name]
+    B, H, Nq, Nk, d, dv, off, causal, mult = FP8_GENERAL[name]
     print("case fp8 general %s" % name, flush=True)
     ta = _ta()
     g = torch.Generator().manual_seed(500 + Nq + Nk)
-    q = (torch.randn((B, H, Nq, 128), generator=g) * mult).to(torch.bfloat16).contiguous()
-    k = (torch.randn((B, H, Nk, 128), generator=g) * mult).to(torch.bfloat16).contiguous()
+    q = (torch.randn((B, H, Nq, d), generator=g) * mult).to(torch.bfloat16).contiguous()
+    k = (torch.randn((B, H, Nk, d), generator=g) * mult).to(torch.bfloat16).contiguous()
     v = torch.randn((B, H, Nk, dv), generator=g).to(torch.bfloat16).contiguous()
-    scale = 1 / np.sqrt(128)
+    scale = 1 / np.sqrt(d)
     q8, qd = ta.attn_quantize_fp8(q.to(DEV))
     if Nk:
         k8, kd = ta.attn_quantize_fp8(k.to(DEV))
     else:
-        k8 = torch.empty((B, H, 0, 128), dtype=torch.uint8, device=DEV)
+        k8 = torch.empty((B, H, 0, d), dtype=torch.uint8, device=DEV)
         kd = torch.ones((B, H), dtype=torch.float32, device=DEV)
     o, lse = ta.attn_fwd_fp8_ex(q8, k8, v.to(DEV), qd, kd, scale=scale, causal=causal,
                                 query_offset=off)
@@ -279,21 +313,20 @@ def test_fp8_general_shapes(name):
         for h in range(H):
             ro, rl = attention_ref(qf[b, h], kf[b, h], vf[b, h], f32_scale(scale), causal,
                                    query_offset=off)
-            amag = abs(f32_scale(scale)) * (np.abs(qf[b, h]) @ np.abs(kf[b, h]).T)
-            if causal:
-                vis = np.arange(Nk)[None, :] <= (np.arange(Nq) + off)[:, None]
-                amag = np.where(vis, amag, 0.0)
-            bars.append(1e-3 + SCORE_TOL * amag.max(axis=1))
+            vis = (np.arange(Nk)[None, :] <= (np.arange(Nq) + off)[:, None]) if causal else None
+            bars.append(_lse_bar(qf[b, h], kf[b, h], scale, vis))
             errs_o.append(np.abs(o[b, h] - ro).ravel())
             errs_l.append(np.abs(lse[b, h] - rl))
     _check(np.concatenate(errs_o), np.concatenate(errs_l), np.concatenate(bars))
 
 
-def test_fp8_ex_square_equals_attn_fwd_fp8():
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_ex_square_equals_attn_fwd_fp8(d):
     """On a square problem with offset 0 the general instance gives the square
     instance's results bit for bit."""
     ta = _ta()
-    q, k, v = make_qkv(2, 2, 333, 128, 95, 4.0)
+    print("case fp8 ex vs square d=%d" % d, flush=True)
+    q, k, v = make_qkv(2, 2, 333, d, 95, 4.0)
     q8, qd = ta.attn_quantize_fp8(q.to(DEV))
     k8, kd = ta.attn_quantize_fp8(k.to(DEV))
     a = ta.attn_fwd_fp8(q8, k8, v.to(DEV), qd, kd, causal=True)

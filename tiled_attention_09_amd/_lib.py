@@ -543,7 +543,7 @@ def attn_fwd_fp8(q8, k8, v, q_descale, k_descale, scale: float | None = None, ca
 
 def attn_fwd_fp8_ex(q8, k8, v, q_descale, k_descale, scale: float | None = None, causal=False,
                     query_offset: int = 0, out=None, lse=None, stream=None):
-    """``attn_fwd_fp8`` for general shapes: q8 [B, H, Nq, 128], k8 [B, H, Nk, 128]
+    """``attn_fwd_fp8`` for general shapes: q8 [B, H, Nq, d], k8 [B, H, Nk, d]
     E4M3 codes, v bf16 [B, H, Nk, dv], descales float32 [B, H]; query r at
     position query_offset + r.  Returns (o [B, H, Nq, dv], lse [B, H, Nq])."""
     import torch

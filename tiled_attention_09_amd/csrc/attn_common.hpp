@@ -36,7 +36,9 @@ constexpr float kLn2 = 0.69314718055994530942f;
 
 template <int D>
 struct Tile {
-  static_assert(D == 64 || D == 128, "head dim");
+  // 64 and 128: bf16 rows of Q, K, V.  32: the geometry of the 64-byte rows of
+  // FP8 codes at d = 64 (a bf16 row of 32 values is 64 bytes).
+  static_assert(D == 32 || D == 64 || D == 128, "row width");
   static constexpr int KS = D / 16;                 // MFMA k-steps over d for S^T
   static constexpr int DB = D / 32;                 // 32-row blocks of O^T
   static constexpr int DCH = D / 8;                 // 16-byte chunks per key row
@@ -48,10 +50,13 @@ struct Tile {
   // on any 16 aligned rows, and rows 4a..4a+3 get 4 different 64-byte groups.
   // d=64 (8 chunks, two rows per 256-byte bank window): bijective on the rows
   // of one parity within 16 rows, and rows 4a, 4a+2 (and 4a+1, 4a+3) get
-  // different 64-byte groups.
+  // different 64-byte groups.  32 (4 chunks of 16 bytes, four rows per
+  // 256-byte bank window): rows r and r + 4 k differ in (r >> 2) & 3, so 16
+  // consecutive rows at one chunk index fill 16 different 16-byte slots.
   __device__ static __forceinline__ int swz(int r) {
     if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+    else if constexpr (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+    else return (r >> 2) & 3;
   }
 };
 
@@ -322,19 +327,23 @@ struct LdsReader {
 };
 
 // A operands of the FP8 score product (v_mfma_scale_f32_32x32x64_f8f6f4) from
-// a tile of 128-byte rows (128 FP8 values; the geometry and swizzle of a bf16
-// Tile<64>): row 32 rb + l32, bytes [64 ks + 32 hi, +32) as two 16-byte reads.
-// Both operands of the product use this byte order, so the k order inside the
-// instruction does not matter.  Chunk indices 4 ks + 2 hi + part have disjoint
-// bits, so the swizzle is one per-lane XOR with a compile-time constant.
+// a tile of ROWB-byte rows (ROWB FP8 values: 128 with the geometry and swizzle
+// of a bf16 Tile<64>, 64 with that of a Tile<32>): row 32 rb + l32, bytes
+// [64 ks + 32 hi, +32) as two 16-byte reads.  Both operands of the product use
+// this byte order, so the k order inside the instruction does not matter.
+// Chunk indices 4 ks + 2 hi + part have disjoint bits, so the swizzle is one
+// per-lane XOR with a compile-time constant.
+template <int ROWB>
 struct LdsReaderF8 {
+  static_assert(ROWB == 64 || ROWB == 128, "FP8 row bytes");
+  using TG = Tile<ROWB / 2>;   // the bf16 tile with the same row geometry
   uint32_t rows;
   __device__ __forceinline__ explicit LdsReaderF8(int lane) {
     const int l32 = lane & 31, hi = lane >> 5;
-    rows = (uint32_t)(l32 * 128) | ((uint32_t)((2 * hi) ^ Tile<64>::swz(l32)) << 4);
+    rows = (uint32_t)(l32 * ROWB) | ((uint32_t)((2 * hi) ^ TG::swz(l32)) << 4);
   }
   __device__ __forceinline__ i32x8 row_op(const TA_LDS uint8_t* t, int rb, int ks) const {
-    const TA_LDS char* base = (const TA_LDS char*)t + rb * 32 * 128;
+    const TA_LDS char* base = (const TA_LDS char*)t + rb * 32 * ROWB;
     const u32x4 a = *reinterpret_cast<const TA_LDS u32x4*>(base + (rows ^ (uint32_t)((4 * ks) << 4)));
     const u32x4 b = *reinterpret_cast<const TA_LDS u32x4*>(base + (rows ^ (uint32_t)((4 * ks + 1) << 4)));
     return __builtin_bit_cast(i32x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));

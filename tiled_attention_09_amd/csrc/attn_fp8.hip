@@ -16,7 +16,7 @@ constexpr int kMaxN = 1 << 22;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-template <int DV, bool CAUSAL, bool GENERAL>
+template <int D, int DV, bool CAUSAL, bool GENERAL>
 int launch_fp8(const void* q8, const void* k8, const void* v, float* o, float* lse,
                const float* qd, const float* kd, int bh, int Nq, int Nk, int offset,
                float scale_log2, hipStream_t stream) {
@@ -25,24 +25,24 @@ int launch_fp8(const void* q8, const void* k8, const void* v, float* o, float* l
   const dim3 block(tiledattn::kThreads);
   const uint16_t* vv = static_cast<const uint16_t*>(v);
   if (scale_log2 > 0.f)
-    tiledattn::attn_fwd_kernel<128, DV, CAUSAL, true, GENERAL, true><<<grid, block, 0, stream>>>(
+    tiledattn::attn_fwd_kernel<D, DV, CAUSAL, true, GENERAL, true><<<grid, block, 0, stream>>>(
         q8, k8, vv, o, lse, bh, Nq, Nk, offset, n_qt, scale_log2, qd, kd, tiledattn::DropoutArgs{},
         bh, 0);
   else
-    tiledattn::attn_fwd_kernel<128, DV, CAUSAL, false, GENERAL, true><<<grid, block, 0, stream>>>(
+    tiledattn::attn_fwd_kernel<D, DV, CAUSAL, false, GENERAL, true><<<grid, block, 0, stream>>>(
         q8, k8, vv, o, lse, bh, Nq, Nk, offset, n_qt, scale_log2, qd, kd, tiledattn::DropoutArgs{},
         bh, 0);
   return hipGetLastError() == hipSuccess ? TA_OK : TA_ERR_HIP;
 }
 
-template <int DV, bool GENERAL>
+template <int D, int DV, bool GENERAL>
 int launch_fp8_mask(const void* q8, const void* k8, const void* v, float* o, float* lse,
                     const float* qd, const float* kd, int bh, int Nq, int Nk, int offset,
                     float scale_log2, int causal, hipStream_t s) {
-  return causal ? launch_fp8<DV, true, GENERAL>(q8, k8, v, o, lse, qd, kd, bh, Nq, Nk, offset,
-                                                scale_log2, s)
-                : launch_fp8<DV, false, GENERAL>(q8, k8, v, o, lse, qd, kd, bh, Nq, Nk, offset,
-                                                 scale_log2, s);
+  return causal ? launch_fp8<D, DV, true, GENERAL>(q8, k8, v, o, lse, qd, kd, bh, Nq, Nk,
+                                                   offset, scale_log2, s)
+                : launch_fp8<D, DV, false, GENERAL>(q8, k8, v, o, lse, qd, kd, bh, Nq, Nk,
+                                                    offset, scale_log2, s);
 }
 
 }  // namespace
@@ -54,7 +54,7 @@ extern "C" int attn_fwd_fp8(const void* q8, const void* k8, const void* v, float
   if (B < 1 || H < 1 || N < 1 || N > kMaxN) return TA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return TA_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return TA_ERR_INVALID_ARG;
-  if (d != 128) return TA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return TA_ERR_UNSUPPORTED;
   if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(lse, 4) || !aligned(q_descale, 4) || !aligned(k_descale, 4))
     return TA_ERR_MISALIGNED;
@@ -63,8 +63,10 @@ extern "C" int attn_fwd_fp8(const void* q8, const void* k8, const void* v, float
   if (bh * n_qt > INT32_MAX) return TA_ERR_INVALID_ARG;
   const float scale_log2 = (float)((double)scale * 1.4426950408889634073599);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return launch_fp8_mask<128, false>(q8, k8, v, o, lse, q_descale, k_descale, (int)bh, N, N, 0,
-                                     scale_log2, causal, s);
+  return d == 64 ? launch_fp8_mask<64, 64, false>(q8, k8, v, o, lse, q_descale, k_descale,
+                                                  (int)bh, N, N, 0, scale_log2, causal, s)
+                 : launch_fp8_mask<128, 128, false>(q8, k8, v, o, lse, q_descale, k_descale,
+                                                    (int)bh, N, N, 0, scale_log2, causal, s);
 }
 
 extern "C" int attn_fwd_fp8_ex(const void* q8, const void* k8, const void* v, float* o,
@@ -78,7 +80,7 @@ extern "C" int attn_fwd_fp8_ex(const void* q8, const void* k8, const void* v, fl
   if (query_offset < 0 || query_offset > (1 << 30)) return TA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return TA_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return TA_ERR_INVALID_ARG;
-  if (d != 128 || (dv != 64 && dv != 128)) return TA_ERR_UNSUPPORTED;
+  if ((d != 64 && d != 128) || (dv != 64 && dv != 128)) return TA_ERR_UNSUPPORTED;
   if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(lse, 4) || !aligned(q_descale, 4) || !aligned(k_descale, 4))
     return TA_ERR_MISALIGNED;
@@ -88,10 +90,16 @@ extern "C" int attn_fwd_fp8_ex(const void* q8, const void* k8, const void* v, fl
   if (Nq == 0) return TA_OK;
   const float scale_log2 = (float)((double)scale * 1.4426950408889634073599);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return dv == 64 ? launch_fp8_mask<64, true>(q8, k8, v, o, lse, q_descale, k_descale, (int)bh, Nq,
-                                              Nk, query_offset, scale_log2, causal, s)
-                  : launch_fp8_mask<128, true>(q8, k8, v, o, lse, q_descale, k_descale, (int)bh,
-                                               Nq, Nk, query_offset, scale_log2, causal, s);
+  const int bhi = (int)bh;
+  if (d == 64)
+    return dv == 64 ? launch_fp8_mask<64, 64, true>(q8, k8, v, o, lse, q_descale, k_descale, bhi,
+                                                    Nq, Nk, query_offset, scale_log2, causal, s)
+                    : launch_fp8_mask<64, 128, true>(q8, k8, v, o, lse, q_descale, k_descale, bhi,
+                                                     Nq, Nk, query_offset, scale_log2, causal, s);
+  return dv == 64 ? launch_fp8_mask<128, 64, true>(q8, k8, v, o, lse, q_descale, k_descale, bhi,
+                                                   Nq, Nk, query_offset, scale_log2, causal, s)
+                  : launch_fp8_mask<128, 128, true>(q8, k8, v, o, lse, q_descale, k_descale, bhi,
+                                                    Nq, Nk, query_offset, scale_log2, causal, s);
 }
 
 extern "C" int attn_quantize_fp8(const void* x, void* out, float* descale, int heads, int rows,

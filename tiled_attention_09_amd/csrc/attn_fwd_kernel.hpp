@@ -70,7 +70,7 @@ constexpr int kDropValuPerMfma = 16;
 // GENERAL = false is the square case (Nk = Nq, offset 0) with those facts
 // known at compile time.  F8: Q and K are FP8 (OCP E4M3) codes with per-head
 // descale factors (Q = codes * q_descale[b h], likewise K), the scores use the
-// FP8 matrix product, and the descales fold into the exponent scale (d = 128).
+// FP8 matrix product, and the descales fold into the exponent scale (d = 64 or 128).
 // DROPOUT: each probability is kept or zeroed by the reproducible mask of
 // `drop` (DropoutArgs) and the output scaled by keep_scale; the normaliser and
 // LSE count every visible key; the mask's row counter is the query's absolute
@@ -88,16 +88,17 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
                      int n_qt, float scale_log2, const float* __restrict__ q_descale,
                      const float* __restrict__ k_descale, DropoutArgs drop, int heads,
                      int split_tiles) {
-  static_assert(!F8 || D == 128, "FP8 scores: d = 128");
+  static_assert(!F8 || D == 64 || D == 128, "FP8 scores: d = 64 or 128");
   static_assert(!DROPOUT || !F8, "dropout: bf16 scores");
   static_assert(!SPLIT || (GENERAL && !F8 && !DROPOUT), "split key ranges: general bf16 shapes");
   const int Nk = GENERAL ? nk_arg : Nq;
   const int offset = GENERAL ? offset_arg : 0;
   using T = Tile<D>;
   using TV = Tile<DV>;
-  // K tile geometry in bytes: an FP8 row of 128 values is laid out like a
-  // bf16 row of 64 (128 bytes, 8 chunks).
-  using TK = Tile<F8 ? 64 : D>;
+  // K tile geometry in bytes: an FP8 row of D values is laid out like a bf16
+  // row of D / 2 (D bytes).
+  constexpr int DK = F8 ? D / 2 : D;
+  using TK = Tile<DK>;
   constexpr uint32_t kElemQK = F8 ? 1u : 2u;     // bytes per Q / K value
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[TK::BYTES];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[kBN * DV];
@@ -161,12 +162,12 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
 
   // Tile copy offsets: the same for every tile (K and V differ only when D != DV).
   uint32_t src_k[TK::LOADS], src_v[TV::LOADS];
-  tile_src_offsets<F8 ? 64 : D>(src_k, wave, lane);
+  tile_src_offsets<DK>(src_k, wave, lane);
   tile_src_offsets<DV>(src_v, wave, lane);
   // Operand reads: K row-wise (A operand of S^T), V transposed (A operand of
   // O^T), with lane offsets whose row/stage parts fold into the instruction.
   const LdsReader<D> rd(lane);
-  const LdsReaderF8 rd8(lane);
+  const LdsReaderF8<D> rd8(lane);
   const LdsReader<DV> rdv(lane);
 
   f32x16 oacc[TV::DB];
@@ -385,7 +386,7 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();                 // K_{j+1}, V_j visible; K_j, V_{j-1} stages free
     if (j + 2 < n_kt)
-      issue_rows<F8 ? 64 : D>(kr, src_k, j + 2, wave, (TA_LDS uint16_t*)(P ? k1 : k0));
+      issue_rows<DK>(kr, src_k, j + 2, wave, (TA_LDS uint16_t*)(P ? k1 : k0));
     if (j + 1 < n_kt) issue_rows<DV>(vr, src_v, j + 1, wave, P ? v0 : v1);
     if (j < n_w) {
       if constexpr (P == 0)
@@ -396,9 +397,9 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
   };
 
   if (n_kt > kt_lo) {
-    issue_rows<F8 ? 64 : D>(kr, src_k, kt_lo, wave, (TA_LDS uint16_t*)k0);
+    issue_rows<DK>(kr, src_k, kt_lo, wave, (TA_LDS uint16_t*)k0);
     issue_rows<DV>(vr, src_v, kt_lo, wave, v0);
-    if (n_kt > kt_lo + 1) issue_rows<F8 ? 64 : D>(kr, src_k, kt_lo + 1, wave, (TA_LDS uint16_t*)k1);
+    if (n_kt > kt_lo + 1) issue_rows<DK>(kr, src_k, kt_lo + 1, wave, (TA_LDS uint16_t*)k1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (n_w > kt_lo) scores(k0, sa);
