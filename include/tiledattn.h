@@ -234,7 +234,8 @@ int attn_fwd_dropout_ex(const void* q, const void* k, const void* v, float* o, f
 
 /*
  * attn_bwd_workspace_size -- bytes of device workspace attn_bwd needs for
- * (B, H, N): 8 * B * H * (N rounded up to even); for attn_bwd_ex pass N = Nq.
+ * (B, H, N): 8 * B * H * (N rounded up to a multiple of 4); for attn_bwd_ex pass
+ * N = Nq.
  * Returns 0 when the sizes are out of the range the backward accepts (N = 0
  * gives 0 bytes, valid for attn_bwd_ex only).
  */
@@ -342,7 +343,7 @@ int attn_bwd_dropout_ex(const void* q, const void* k, const void* v, const float
  * a caller workspace.  The call allocates nothing, neither does the library.
  *
  *   scratch : a fixed 16 MiB array per device, held until the process ends;
- *             it needs 8 * B * H * (N rounded up to even) bytes, so
+ *             it needs 8 * B * H * (N rounded up to a multiple of 4) bytes, so
  *             B * H * N <= 2^21 rows (sizes beyond it: TA_ERR_TOO_LARGE,
  *             before any HIP call).  Nothing in it needs to start at zero.
  *   Every call on one device shares that device's scratch: calls that may

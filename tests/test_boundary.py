@@ -132,8 +132,9 @@ def call_bwd(**over):
 
 def test_workspace_size():
     assert ta.attn_bwd_workspace_size(2, 32, 8192) == 2 * 32 * 8192 * 8
-    assert ta.attn_bwd_workspace_size(1, 1, 1003) == 1004 * 8    # rows padded to even
-    assert ta.attn_bwd_workspace_size(3, 5, 1) == 15 * 2 * 8
+    assert ta.attn_bwd_workspace_size(1, 1, 1003) == 1004 * 8    # rows padded to a multiple of 4
+    assert ta.attn_bwd_workspace_size(1, 1, 1001) == 1004 * 8
+    assert ta.attn_bwd_workspace_size(3, 5, 1) == 15 * 4 * 8
     assert ta.attn_bwd_workspace_size(0, 1, 8) == 0
     assert ta.attn_bwd_workspace_size(1, 1, (1 << 22) + 1) == 0
 
@@ -439,10 +440,10 @@ def noalloc(**over):
 
 @host_only
 def test_noalloc_rejects_sizes_beyond_its_scratch():
-    """16 MiB of scratch holds 8 bytes per row of B*H*(N rounded up to even): 2^21 rows."""
+    """16 MiB of scratch holds 8 bytes per row of B*H*(N rounded up to a multiple of 4): 2^21 rows."""
     assert noalloc(B=1, H=1, N=(1 << 21) + 2) == ta.TA_ERR_TOO_LARGE
     assert noalloc(B=2, H=16, N=65538) == ta.TA_ERR_TOO_LARGE
-    assert noalloc(B=64, H=1, N=32769) == ta.TA_ERR_TOO_LARGE      # rounded up to 32770 rows
+    assert noalloc(B=64, H=1, N=32769) == ta.TA_ERR_TOO_LARGE      # rounded up to 32772 rows
 
 
 @host_only

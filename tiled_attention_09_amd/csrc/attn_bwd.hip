@@ -21,8 +21,9 @@ constexpr int kMaxOffset = 1 << 30;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// Rows of one head in the workspace, padded to an even count (16-byte heads).
-int64_t stats_stride(int N) { return ((int64_t)N + 1) & ~(int64_t)1; }
+// Rows of one head's statistics planes, padded to a multiple of 4 (each
+// plane 16-byte aligned).
+int64_t stats_stride(int N) { return ((int64_t)N + 3) & ~(int64_t)3; }
 
 struct Shape {
   int bh, Nq, Nk, offset;
@@ -31,7 +32,7 @@ struct Shape {
 template <int D, int DV, bool CAUSAL, bool GENERAL, bool DROPOUT>
 int launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* o,
            const float* lse, const uint16_t* g, float* dq, float* dk, float* dv,
-           tiledattn::f32x2* stats, Shape sh, float scale, tiledattn::DropoutArgs dr,
+           float* stats, Shape sh, float scale, tiledattn::DropoutArgs dr,
            hipStream_t stream) {
   using namespace tiledattn;
   const int stride = (int)stats_stride(sh.Nq);
@@ -65,7 +66,7 @@ int launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float*
 template <int D, int DV, bool GENERAL, bool DROPOUT>
 int launch_mask(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* o,
                 const float* lse, const uint16_t* g, float* dq, float* dk, float* dv,
-                tiledattn::f32x2* st, Shape sh, float scale, int causal,
+                float* st, Shape sh, float scale, int causal,
                 tiledattn::DropoutArgs dr, hipStream_t s) {
   return causal ? launch<D, DV, true, GENERAL, DROPOUT>(q, k, v, o, lse, g, dq, dk, dv, st, sh,
                                                         scale, dr, s)
@@ -123,7 +124,7 @@ int backward(const void* q, const void* k, const void* v, const float* o, const 
   auto* kk = static_cast<const uint16_t*>(k);
   auto* vv = static_cast<const uint16_t*>(v);
   auto* gg = static_cast<const uint16_t*>(dout);
-  auto* st = static_cast<tiledattn::f32x2*>(workspace);
+  auto* st = static_cast<float*>(workspace);
   if (square)
     return d == 64 ? launch_mask<64, 64, false, DROPOUT>(qq, kk, vv, o, lse, gg, dq, dk, dv, st,
                                                          sh, scale, causal, dr, s)

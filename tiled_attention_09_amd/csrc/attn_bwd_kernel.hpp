@@ -14,9 +14,8 @@
 // and K rows of width D, V, O and G rows of width DV.
 //
 // Three kernels, all on the caller's stream:
-//  1. attn_bwd_prep_kernel: per row, D and LSE2 into a workspace of float2
-//     {LSE2, D}, each head's rows padded to an even count so every head starts
-//     16-byte aligned (HBM-bound, one pass over O and G).
+//  1. attn_bwd_prep_kernel: per row, LSE2 and -D into a workspace of two
+//     planes per head (HBM-bound, one pass over O and G).
 //  2. attn_bwd_dkdv_kernel: one workgroup owns 128 keys of one head (32 per
 //     wave) and streams that head's query rows in tiles of 64; the wave's dK
 //     and dV rows stay in registers for the whole loop and are written once,
@@ -53,26 +52,38 @@
 
 namespace tiledattn {
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
 constexpr int kPrepRowsPerBlock = 16;     // 16 lanes per row, 256 threads
 
-// Copy the {LSE2, D} pairs of the 64 query rows of tile i (512 bytes) into LDS:
-// lanes 0..31 of wave 0, 16 bytes each.
-__device__ __forceinline__ void issue_stats(__amdgpu_buffer_rsrc_t sr, int i, int wave, int lane,
-                                            TA_LDS float* sd) {
-  if (wave == 0 && lane < 32)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (TA_LDS void*)sd, 16, (uint32_t)lane * 16u,
-                                             (uint32_t)i * (kBN * 8u), 0, 0);
+// Row statistics workspace: per head two planes of `stride` floats (stride:
+// the rows rounded up to a multiple of 4, so both planes start 16-byte
+// aligned): LSE2 of every row, then -D of every row (the starting value of a
+// dP accumulator, so the products yield dP - D directly).
+//
+// Copy LSE2 and -D of the 64 query rows of tile i into LDS (256 bytes each,
+// -D after LSE2): lanes 0..15 of wave 0 copy the LSE2 rows, lanes 16..31 the
+// -D rows, 16 bytes each.  Each plane has a buffer resource of its own
+// covering Nq rows, so rows past the end read as zeros (a finite D keeps the
+// masked products finite).
+__device__ __forceinline__ void issue_stats(__amdgpu_buffer_rsrc_t srl, __amdgpu_buffer_rsrc_t srd,
+                                            int i, int wave, int lane, TA_LDS float* sd) {
+  if (wave == 0) {
+    if (lane < 16)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(srl, (TA_LDS void*)sd, 16, (uint32_t)lane * 16u,
+                                               (uint32_t)i * (kBN * 4u), 0, 0);
+    else if (lane < 32)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(srd, (TA_LDS void*)sd, 16,
+                                               (uint32_t)(lane - 16) * 16u,
+                                               (uint32_t)i * (kBN * 4u), 0, 0);
+  }
 }
 
 // ---------------------------------------------------------------------------
-// 1. D_i = sum_c G[i,c] O[i,c] and LSE2_i = LSE_i log2(e), one row per 16 lanes.
+// 1. -D_i = -sum_c G[i,c] O[i,c] and LSE2_i = LSE_i log2(e), one row per 16 lanes.
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const float* __restrict__ O,
                                                             const uint16_t* __restrict__ G,
                                                             const float* __restrict__ LSE,
-                                                            f32x2* __restrict__ stats, int N,
+                                                            float* __restrict__ stats, int N,
                                                             int stats_stride, int64_t rows) {
   constexpr int E = D / 16;                      // values per lane: 8 (d=128) or 4 (d=64)
   const int sub = threadIdx.x & 15;
@@ -96,10 +107,9 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const float* __restr
   for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
   if (row < rows && sub == 0) {
     const int64_t bh = row / N;
-    f32x2 st;
-    st[0] = LSE[row] * kLog2e;
-    st[1] = acc;
-    stats[bh * stats_stride + (row - bh * N)] = st;
+    float* head = stats + bh * 2 * stats_stride;
+    head[row - bh * N] = LSE[row] * kLog2e;
+    head[stats_stride + (row - bh * N)] = -acc;
   }
 }
 
@@ -167,7 +177,7 @@ template <int D, int DV, bool CAUSAL, bool GENERAL, bool DROPOUT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ G,
-                          const f32x2* __restrict__ stats, float* __restrict__ dK,
+                          const float* __restrict__ stats, float* __restrict__ dK,
                           float* __restrict__ dV, int bh_count, int Nq, int nk_arg,
                           int offset_arg, int stats_stride, int n_kt, float c, float scale,
                           int skip_floor, DropoutArgs drop) {
@@ -180,7 +190,7 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   __shared__ __attribute__((aligned(1024))) uint16_t g_lds0[kBN * DV];
   __shared__ __attribute__((aligned(1024))) uint16_t q_lds1[kBN * D];
   __shared__ __attribute__((aligned(1024))) uint16_t g_lds1[kBN * DV];
-  __shared__ __attribute__((aligned(16))) float st_lds0[2 * kBN];   // {LSE2, D} per query row
+  __shared__ __attribute__((aligned(16))) float st_lds0[2 * kBN];   // LSE2 rows, then -D rows
   __shared__ __attribute__((aligned(16))) float st_lds1[2 * kBN];
   __shared__ __attribute__((aligned(16))) uint32_t mk_lds[DROPOUT ? kWaves * 32 * 16 : 4];
 
@@ -198,7 +208,9 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   const __amdgpu_buffer_rsrc_t gr = make_rsrc(G + qhead * DV, (uint32_t)Nq * DV * 2u);
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(K + khead * D, (uint32_t)Nk * D * 2u);
   const __amdgpu_buffer_rsrc_t vr = make_rsrc(V + khead * DV, (uint32_t)Nk * DV * 2u);
-  const __amdgpu_buffer_rsrc_t sr = make_rsrc(stats + (size_t)bh * stats_stride, (uint32_t)Nq * 8u);
+  const float* st_head = stats + (size_t)bh * 2 * (size_t)stats_stride;
+  const __amdgpu_buffer_rsrc_t srl = make_rsrc(st_head, (uint32_t)Nq * 4u);
+  const __amdgpu_buffer_rsrc_t srd = make_rsrc(st_head + stats_stride, (uint32_t)Nq * 4u);
 
   const int k0 = kt * kBM + wave * 32;    // first key of this wave
   const int my_k = k0 + l32;              // this lane's key
@@ -238,12 +250,13 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
                           const TA_LDS float* st) {
     const int qbase = i * kBN;
     // Row statistics of the 16 query rows each lane holds per block: element
-    // 4 g4 + t of block qb is tile row 32 qb + 8 g4 + 4 hi + t.  LSE2 is kept
-    // for the exponent; -D is the starting value of the dP accumulator, so the
-    // products below yield dP - D directly.
+    // 4 g4 + t of block qb is tile row 32 qb + 8 g4 + 4 hi + t (four
+    // consecutive rows, one 16-byte read per plane).  LSE2 is kept for the
+    // exponent; the stored -D is the starting value of the dP accumulator, so
+    // the products below yield dP - D directly.
     f32x16 s[2], dp[2];
     float lse2[2][16];
-    float dd[DROPOUT ? 2 : 1][16];   // dropout: D itself, the dP accumulator starts at 0
+    float nd[DROPOUT ? 2 : 1][16];   // dropout: -D itself, the dP accumulator starts at 0
     uint32_t mk[2][4];
     if constexpr (DROPOUT)
       dropout_col_words((uint32_t)(qbase + offset), (uint32_t)k0, (uint32_t)bh, drop, lane,
@@ -252,24 +265,17 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     for (int r = 0; r < 8; ++r) {
       const int qb = r >> 2, g4 = r & 3;
       const int qrow = 32 * qb + 8 * g4 + 4 * hi;
-      const f32x4 a = *reinterpret_cast<const TA_LDS f32x4*>(st + 2 * qrow);
-      const f32x4 b = *reinterpret_cast<const TA_LDS f32x4*>(st + 2 * qrow + 4);
-      lse2[qb][4 * g4 + 0] = a[0];
-      lse2[qb][4 * g4 + 1] = a[2];
-      lse2[qb][4 * g4 + 2] = b[0];
-      lse2[qb][4 * g4 + 3] = b[2];
-      if constexpr (DROPOUT) {
-        dd[qb][4 * g4 + 0] = a[1];
-        dd[qb][4 * g4 + 1] = a[3];
-        dd[qb][4 * g4 + 2] = b[1];
-        dd[qb][4 * g4 + 3] = b[3];
+      const f32x4 l2 = *reinterpret_cast<const TA_LDS f32x4*>(st + qrow);
+      const f32x4 n = *reinterpret_cast<const TA_LDS f32x4*>(st + kBN + qrow);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) dp[qb][4 * g4 + t] = 0.f;
-      } else {
-        dp[qb][4 * g4 + 0] = -a[1];
-        dp[qb][4 * g4 + 1] = -a[3];
-        dp[qb][4 * g4 + 2] = -b[1];
-        dp[qb][4 * g4 + 3] = -b[3];
+      for (int t = 0; t < 4; ++t) {
+        lse2[qb][4 * g4 + t] = l2[t];
+        if constexpr (DROPOUT) {
+          nd[qb][4 * g4 + t] = n[t];
+          dp[qb][4 * g4 + t] = 0.f;
+        } else {
+          dp[qb][4 * g4 + t] = n[t];
+        }
       }
     }
     // S and dP - D: 2 blocks of 32 queries x the wave's 32 keys (4 KS products).
@@ -321,8 +327,8 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
           // dV uses P M (keep_scale is applied to dV once, at the end).
           const bool keep = dropout_keep(mk, qb, e, drop.t);
           pf[2 * qb + (e >> 3)][e & 7] = (__bf16)(keep ? p : 0.f);
-          const float g = keep ? __builtin_fmaf(drop.keep_scale, dp[qb][e], -dd[qb][e])
-                               : -dd[qb][e];
+          const float g = keep ? __builtin_fmaf(drop.keep_scale, dp[qb][e], nd[qb][e])
+                               : nd[qb][e];
           sf[2 * qb + (e >> 3)][e & 7] = (__bf16)(p * g);
         } else {
           pf[2 * qb + (e >> 3)][e & 7] = (__bf16)p;
@@ -366,20 +372,20 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
   // after it, so the loop has a single exit.
   if (i0 < n_qt) {
     issue_pair<D, DV>(qr, gr, src_q, src_g, i0, wave, q0p, g0p);
-    issue_stats(sr, i0, wave, lane, s0p);
+    issue_stats(srl, srd, i0, wave, lane, s0p);
   }
   int i = i0;
   for (; i + 1 < n_qt; i += 2) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();                       // tile i visible; tile i-1's readers done
     issue_pair<D, DV>(qr, gr, src_q, src_g, i + 1, wave, q1p, g1p);
-    issue_stats(sr, i + 1, wave, lane, s1p);
+    issue_stats(srl, srd, i + 1, wave, lane, s1p);
     if (active(i)) compute_tile(i, q0p, g0p, s0p);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (i + 2 < n_qt) {
       issue_pair<D, DV>(qr, gr, src_q, src_g, i + 2, wave, q0p, g0p);
-      issue_stats(sr, i + 2, wave, lane, s0p);
+      issue_stats(srl, srd, i + 2, wave, lane, s0p);
     }
     if (active(i + 1)) compute_tile(i + 1, q1p, g1p, s1p);
   }
@@ -432,7 +438,7 @@ template <int D, int DV, bool CAUSAL, bool GENERAL, bool DROPOUT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                         const uint16_t* __restrict__ V, const uint16_t* __restrict__ G,
-                        const f32x2* __restrict__ stats, float* __restrict__ dQ, int bh_count,
+                        const float* __restrict__ stats, float* __restrict__ dQ, int bh_count,
                         int Nq, int nk_arg, int offset_arg, int stats_stride, int n_qt, float c,
                         float scale, int skip_ceiling, DropoutArgs drop) {
   static_assert(GENERAL || D == DV, "square instances have one head width");
@@ -471,11 +477,11 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 #pragma unroll
   for (int ks = 0; ks < TV::KS; ++ks)
     gf[ks] = __builtin_bit_cast(bf16x8, load16(gr, (uint32_t)(my_q * DV + 16 * ks + 8 * hi) * 2u));
-  float lse2 = 0.f, dd = 0.f;
+  float lse2 = 0.f, nd = 0.f;   // LSE2 and -D of the lane's query
   if (my_q < Nq) {
-    const f32x2 st = stats[(size_t)bh * stats_stride + my_q];
-    lse2 = st[0];
-    dd = st[1];
+    const float* st_head = stats + (size_t)bh * 2 * (size_t)stats_stride;
+    lse2 = st_head[my_q];
+    nd = st_head[stats_stride + my_q];
   }
 
   uint32_t src_k[T::LOADS], src_v[TV::LOADS];
@@ -536,9 +542,9 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
       bf16x8 sf[2];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        float g = dp[e] - dd;
+        float g = dp[e] + nd;
         if constexpr (DROPOUT)
-          g = dropout_keep(mw, kb, e, drop.t) ? __builtin_fmaf(drop.keep_scale, dp[e], -dd) : -dd;
+          g = dropout_keep(mw, kb, e, drop.t) ? __builtin_fmaf(drop.keep_scale, dp[e], nd) : nd;
         sf[e >> 3][e & 7] = (__bf16)(__builtin_amdgcn_exp2f(s[e]) * g);
       }
 
