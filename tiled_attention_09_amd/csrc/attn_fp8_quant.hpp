@@ -31,8 +31,10 @@ __global__ __launch_bounds__(256) void fp8_amax_init_kernel(uint32_t* amax_bits,
 // Amax pass: each thread reads kAmaxPerThread bf16 values (eight independent
 // 16-byte loads in flight), so a head of 2^20 values takes 64 blocks and the
 // pass streams at HBM rate; one atomic per block.  Grid: (chunks of
-// kAmaxPerBlock values, heads).  n_per_head is a multiple of 64 (rows x d,
-// d = 64 or 128), so a thread's values are all in range or all past the end.
+// kAmaxPerBlock values, heads).  A wave covers 64 kAmaxPerThread consecutive
+// values, load v of lane l the 8 values at 512 v + 8 l of them: every load
+// instruction reads 1 KB contiguous.  n_per_head is a multiple of 8, so each
+// 8-value load is all in range or all past the end.
 constexpr int kAmaxPerThread = 64;
 constexpr int kAmaxPerBlock = kQuantThreads * kAmaxPerThread;
 
@@ -41,18 +43,19 @@ __global__ __launch_bounds__(kQuantThreads) void fp8_amax_kernel(const uint16_t*
                                                                  int64_t n_per_head) {
   __shared__ uint32_t part[kQuantThreads / 64];
   const int64_t base = (int64_t)blockIdx.y * n_per_head;
-  const int64_t i0 = (int64_t)blockIdx.x * kAmaxPerBlock + (int64_t)threadIdx.x * kAmaxPerThread;
+  const int lane = threadIdx.x & 63;
+  const int64_t w0 = (int64_t)blockIdx.x * kAmaxPerBlock + (int64_t)(threadIdx.x >> 6) * (64 * kAmaxPerThread);
   uint32_t m = 0u;   // |x| as bits: bf16 bits << 16 with the sign cleared
-  if (i0 < n_per_head) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(x + base + i0);
-    u32x4 w[kAmaxPerThread / 8];
+  u32x4 w[kAmaxPerThread / 8];
 #pragma unroll
-    for (int v = 0; v < kAmaxPerThread / 8; ++v) w[v] = src[v];
-#pragma unroll
-    for (int v = 0; v < kAmaxPerThread / 8; ++v)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) m = max(m, max((w[v][t] << 16) & 0x7fffffffu, w[v][t] & 0x7fff0000u));
+  for (int v = 0; v < kAmaxPerThread / 8; ++v) {
+    const int64_t i = w0 + 512 * v + 8 * lane;
+    w[v] = i < n_per_head ? *reinterpret_cast<const u32x4*>(x + base + i) : u32x4{0u, 0u, 0u, 0u};
   }
+#pragma unroll
+  for (int v = 0; v < kAmaxPerThread / 8; ++v)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) m = max(m, max((w[v][t] << 16) & 0x7fffffffu, w[v][t] & 0x7fff0000u));
   // Wave maximum, then the block's four waves through LDS, then one atomic.
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
