@@ -117,7 +117,9 @@ extern "C" int attn_quantize_fp8(const void* x, void* out, float* descale, int h
   const unsigned hb = (unsigned)((heads + 255) / 256);
   tiledattn::fp8_amax_init_kernel<<<dim3(hb), dim3(256), 0, s>>>(bits, heads);
   const int64_t amax_chunks = (n + tiledattn::kAmaxPerBlock - 1) / tiledattn::kAmaxPerBlock;
-  tiledattn::fp8_amax_kernel<<<dim3((unsigned)amax_chunks, (unsigned)heads),
+  const int64_t amax_blocks = amax_chunks < tiledattn::kAmaxBlocksPerHead
+                                  ? amax_chunks : tiledattn::kAmaxBlocksPerHead;
+  tiledattn::fp8_amax_kernel<<<dim3((unsigned)amax_blocks, (unsigned)heads),
                                dim3(tiledattn::kQuantThreads), 0, s>>>(xx, bits, n);
   const dim3 grid((unsigned)chunks, (unsigned)heads);
   tiledattn::fp8_quant_kernel<<<grid, dim3(tiledattn::kQuantThreads), 0, s>>>(

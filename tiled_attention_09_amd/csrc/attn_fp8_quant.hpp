@@ -28,15 +28,18 @@ __global__ __launch_bounds__(256) void fp8_amax_init_kernel(uint32_t* amax_bits,
   if (h < heads) amax_bits[h] = 0u;
 }
 
-// Amax pass: each thread reads kAmaxPerThread bf16 values (eight independent
-// 16-byte loads in flight), so a head of 2^20 values takes 64 blocks and the
-// pass streams at HBM rate; one atomic per block.  Grid: (chunks of
-// kAmaxPerBlock values, heads).  A wave covers 64 kAmaxPerThread consecutive
-// values, load v of lane l the 8 values at 512 v + 8 l of them: every load
-// instruction reads 1 KB contiguous.  n_per_head is a multiple of 8, so each
-// 8-value load is all in range or all past the end.
+// Amax pass: each thread reads kAmaxPerThread bf16 values per chunk of
+// kAmaxPerBlock (eight independent 16-byte loads in flight), and a block
+// strides over the head's chunks, so a head takes at most kAmaxBlocksPerHead
+// blocks and as many atomics on its amax word (atomics on one word serialise
+// in L2).  Grid: (min(chunks, kAmaxBlocksPerHead), heads).  A wave covers 64
+// kAmaxPerThread consecutive values of a chunk, load v of lane l the 8 values
+// at 512 v + 8 l of them: every load instruction reads 1 KB contiguous.
+// n_per_head is a multiple of 8, so each 8-value load is all in range or all
+// past the end.
 constexpr int kAmaxPerThread = 64;
 constexpr int kAmaxPerBlock = kQuantThreads * kAmaxPerThread;
+constexpr int kAmaxBlocksPerHead = 16;
 
 __global__ __launch_bounds__(kQuantThreads) void fp8_amax_kernel(const uint16_t* __restrict__ x,
                                                                  uint32_t* amax_bits,
@@ -44,18 +47,21 @@ __global__ __launch_bounds__(kQuantThreads) void fp8_amax_kernel(const uint16_t*
   __shared__ uint32_t part[kQuantThreads / 64];
   const int64_t base = (int64_t)blockIdx.y * n_per_head;
   const int lane = threadIdx.x & 63;
-  const int64_t w0 = (int64_t)blockIdx.x * kAmaxPerBlock + (int64_t)(threadIdx.x >> 6) * (64 * kAmaxPerThread);
   uint32_t m = 0u;   // |x| as bits: bf16 bits << 16 with the sign cleared
-  u32x4 w[kAmaxPerThread / 8];
+  for (int64_t c0 = (int64_t)blockIdx.x * kAmaxPerBlock; c0 < n_per_head;
+       c0 += (int64_t)gridDim.x * kAmaxPerBlock) {
+    const int64_t w0 = c0 + (int64_t)(threadIdx.x >> 6) * (64 * kAmaxPerThread);
+    u32x4 w[kAmaxPerThread / 8];
 #pragma unroll
-  for (int v = 0; v < kAmaxPerThread / 8; ++v) {
-    const int64_t i = w0 + 512 * v + 8 * lane;
-    w[v] = i < n_per_head ? *reinterpret_cast<const u32x4*>(x + base + i) : u32x4{0u, 0u, 0u, 0u};
+    for (int v = 0; v < kAmaxPerThread / 8; ++v) {
+      const int64_t i = w0 + 512 * v + 8 * lane;
+      w[v] = i < n_per_head ? *reinterpret_cast<const u32x4*>(x + base + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int v = 0; v < kAmaxPerThread / 8; ++v)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) m = max(m, max((w[v][t] << 16) & 0x7fffffffu, w[v][t] & 0x7fff0000u));
   }
-#pragma unroll
-  for (int v = 0; v < kAmaxPerThread / 8; ++v)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) m = max(m, max((w[v][t] << 16) & 0x7fffffffu, w[v][t] & 0x7fff0000u));
   // Wave maximum, then the block's four waves through LDS, then one atomic.
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
