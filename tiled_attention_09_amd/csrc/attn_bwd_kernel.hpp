@@ -318,23 +318,41 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     }
     // P = 2^arg and dS = P (dP - D), rounded to bf16 as B operands.
     bf16x8 pf[4], sf[4];
+    if constexpr (DROPOUT) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(s[qb][e]);
-        if constexpr (DROPOUT) {
-          // dV uses P M (keep_scale is applied to dV once, at the end).
-          const bool keep = dropout_keep(mk, qb, e, drop.t);
-          pf[2 * qb + (e >> 3)][e & 7] = (__bf16)(keep ? p : 0.f);
-          const float g = keep ? __builtin_fmaf(drop.keep_scale, dp[qb][e], nd[qb][e])
-                               : nd[qb][e];
-          sf[2 * qb + (e >> 3)][e & 7] = (__bf16)(p * g);
-        } else {
+        for (int e = 0; e < 16; e += 2) {
+          float pm[2], ds[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const float p = __builtin_amdgcn_exp2f(s[qb][e + u]);
+            // dV uses P M (keep_scale is applied to dV once, at the end).
+            const bool keep = dropout_keep(mk, qb, e + u, drop.t);
+            pm[u] = keep ? p : 0.f;
+            const float g = keep ? __builtin_fmaf(drop.keep_scale, dp[qb][e + u], nd[qb][e + u])
+                                 : nd[qb][e + u];
+            ds[u] = p * g;
+          }
+          // One packed conversion per pair (after the mask's selects the
+          // compiler would otherwise convert each value alone and permute).
+          const bf16x2 bp = __builtin_convertvector(f32x2{pm[0], pm[1]}, bf16x2);
+          const bf16x2 bs = __builtin_convertvector(f32x2{ds[0], ds[1]}, bf16x2);
+          pf[2 * qb + (e >> 3)][e & 7] = bp[0];
+          pf[2 * qb + (e >> 3)][(e & 7) + 1] = bp[1];
+          sf[2 * qb + (e >> 3)][e & 7] = bs[0];
+          sf[2 * qb + (e >> 3)][(e & 7) + 1] = bs[1];
+        }
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = __builtin_amdgcn_exp2f(s[qb][e]);
           pf[2 * qb + (e >> 3)][e & 7] = (__bf16)p;
           sf[2 * qb + (e >> 3)][e & 7] = (__bf16)(p * dp[qb][e]);
         }
-      }
+    }
 
     // dV^T (dv x 32 keys) += G^T (dv x 64 queries) P;  dK^T (d x 32) += Q^T dS.
     constexpr int DBM = T::DB > TG::DB ? T::DB : TG::DB;

@@ -283,15 +283,30 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float arg = POS_SCALE ? __builtin_fmaf(s[kb][i], scale_log2, -cref) : s[kb][i] - cref;
-        const float p = __builtin_amdgcn_exp2f(arg);
-        if constexpr (kSumInValues) pe[kb * 16 + i] = p;
-        else psum += p;
-        // Dropout zeroes the weight in the value product only: the
-        // normaliser keeps every visible key.
-        const float pv = (DROPOUT && !dropout_keep(mw, kb, i, drop.t)) ? 0.f : p;
-        pf[kb * 2 + (i >> 3)][i & 7] = (__bf16)pv;
+      for (int i = 0; i < 16; i += 2) {
+        float pv[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float arg = POS_SCALE ? __builtin_fmaf(s[kb][i + e], scale_log2, -cref)
+                                      : s[kb][i + e] - cref;
+          const float p = __builtin_amdgcn_exp2f(arg);
+          if constexpr (kSumInValues) pe[kb * 16 + i + e] = p;
+          else psum += p;
+          // Dropout zeroes the weight in the value product only: the
+          // normaliser keeps every visible key.
+          pv[e] = (DROPOUT && !dropout_keep(mw, kb, i + e, drop.t)) ? 0.f : p;
+        }
+        if constexpr (DROPOUT) {
+          // Spelled as one packed conversion per key pair: after the mask's
+          // selects the compiler would otherwise convert each value alone and
+          // pack the halves with a permute.
+          const bf16x2 b = __builtin_convertvector(f32x2{pv[0], pv[1]}, bf16x2);
+          pf[kb * 2 + (i >> 3)][i & 7] = b[0];
+          pf[kb * 2 + (i >> 3)][(i & 7) + 1] = b[1];
+        } else {
+          pf[kb * 2 + (i >> 3)][i & 7] = (__bf16)pv[0];
+          pf[kb * 2 + (i >> 3)][(i & 7) + 1] = (__bf16)pv[1];
+        }
       }
     if constexpr (!kSumInValues) l = __builtin_fmaf(l, alpha, psum);
     return alpha;
