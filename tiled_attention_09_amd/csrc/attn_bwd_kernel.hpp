@@ -528,11 +528,13 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     // its dS^T, then its share of dQ^T.
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      // Without dropout dP^T - D accumulates from -D (the lane's query is the
+      // accumulator column, so every element starts at the same -D).
       f32x16 s, dp;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         s[e] = 0.f;
-        dp[e] = 0.f;
+        dp[e] = DROPOUT ? 0.f : nd;
       }
 #pragma unroll
       for (int ks = 0; ks < T::KS; ++ks) {
@@ -560,7 +562,7 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
       bf16x8 sf[2];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        float g = dp[e] + nd;
+        float g = dp[e];
         if constexpr (DROPOUT)
           g = dropout_keep(mw, kb, e, drop.t) ? __builtin_fmaf(drop.keep_scale, dp[e], nd) : nd;
         sf[e >> 3][e & 7] = (__bf16)(__builtin_amdgcn_exp2f(s[e]) * g);
