@@ -290,15 +290,25 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         const bf16x8 aq = rd.row_op(qt, qb, ks);
         s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ks], s[qb], 0, 0, 0);
       }
+    // The first G operands of dP are read here, under the S products.
+    constexpr int kGPre = 3;
+    bf16x8 agp[kGPre][2];
+#pragma unroll
+    for (int ks = 0; ks < kGPre; ++ks)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) agp[ks][qb] = rdg.row_op(gt, qb, ks);
+    // Statistics and operand reads, 22 ahead, then one after each product.
+    sched_mfma_ds<22, 1, 2 * T::KS + 16 + 2 * kGPre>(std::make_integer_sequence<int, 2 * T::KS>{});
+    // S is issued in full before dP, so that the exponent arguments (accumulator
+    // reads and FMAs, which need only S) run between the dP products.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < TG::KS; ++ks)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const bf16x8 ag = rdg.row_op(gt, qb, ks);
+        const bf16x8 ag = ks < kGPre ? agp[ks < kGPre ? ks : 0][qb] : rdg.row_op(gt, qb, ks);
         dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, vf[ks], dp[qb], 0, 0, 0);
       }
-    sched_mfma_ds<20, 1, 2 * (T::KS + TG::KS) + 16>(
-        std::make_integer_sequence<int, 2 * (T::KS + TG::KS)>{});
 
     // Exponent arguments c s - LSE2; hidden pairs (query before key, or query
     // past the end) get -inf, which exp2 turns into an exact 0.
@@ -307,6 +317,12 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[qb][e] = __builtin_fmaf(s[qb][e], c, -lse2[qb][e]);
+    {
+      constexpr int kDP = 2 * TG::KS;
+      constexpr int kArgPer = (64 + kDP - 1) / kDP;
+      sched_reads<4>();
+      sched_rep<1, kArgPer, kDP>();
+    }
     if (edge) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
