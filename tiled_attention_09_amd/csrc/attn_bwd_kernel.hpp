@@ -261,6 +261,20 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     if constexpr (DROPOUT)
       dropout_col_words((uint32_t)(qbase + offset), (uint32_t)k0, (uint32_t)bh, drop, lane,
                         (TA_LDS uint32_t*)mk_lds + wave * (32 * 16), mk);
+    // S and dP - D: 2 blocks of 32 queries x the wave's 32 keys (4 KS products).
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[qb][e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const bf16x8 aq = rd.row_op(qt, qb, ks);
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ks], s[qb], 0, 0, 0);
+      }
+    // The row statistics (needed from dP on) and the first G operands of dP
+    // are read under the S products, after S's own operands.
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int qb = r >> 2, g4 = r & 3;
@@ -278,27 +292,14 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         }
       }
     }
-    // S and dP - D: 2 blocks of 32 queries x the wave's 32 keys (4 KS products).
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[qb][e] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const bf16x8 aq = rd.row_op(qt, qb, ks);
-        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[ks], s[qb], 0, 0, 0);
-      }
-    // The first G operands of dP are read here, under the S products.
     constexpr int kGPre = 3;
     bf16x8 agp[kGPre][2];
 #pragma unroll
     for (int ks = 0; ks < kGPre; ++ks)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) agp[ks][qb] = rdg.row_op(gt, qb, ks);
-    // Statistics and operand reads, 22 ahead, then one after each product.
-    sched_mfma_ds<22, 1, 2 * T::KS + 16 + 2 * kGPre>(std::make_integer_sequence<int, 2 * T::KS>{});
+    // Reads: 6 ahead, then two after each product.
+    sched_mfma_ds<6, 2, 2 * T::KS + 16 + 2 * kGPre>(std::make_integer_sequence<int, 2 * T::KS>{});
     // S is issued in full before dP, so that the exponent arguments (accumulator
     // reads and FMAs, which need only S) run between the dP products.
     __builtin_amdgcn_sched_barrier(0);
