@@ -293,6 +293,7 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
       }
     }
     constexpr int kGPre = 3;
+    static_assert(TG::KS >= kGPre, "dP has at least kGPre operand steps");
     bf16x8 agp[kGPre][2];
 #pragma unroll
     for (int ks = 0; ks < kGPre; ++ks)
