@@ -254,6 +254,10 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
   // where the vector unit is otherwise idle); the general-shape and dropout
   // instances keep it here (the live p would make them spill).
   constexpr bool kSumInValues = !GENERAL && !DROPOUT;
+  // With the fp32 p kept, its bf16 rounding for the value products also moves
+  // there (each operand converted just before its products): the score region
+  // is bound by the vector unit, the value region is not.
+  constexpr bool kCvtInValues = kSumInValues;
   // Dropout mask words of the tile whose softmax runs next (dropout_row_words).
   uint32_t mw[2][4];
   float pe[32];
@@ -303,7 +307,7 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
           const bf16x2 b = __builtin_convertvector(f32x2{pv[0], pv[1]}, bf16x2);
           pf[kb * 2 + (i >> 3)][i & 7] = b[0];
           pf[kb * 2 + (i >> 3)][(i & 7) + 1] = b[1];
-        } else {
+        } else if constexpr (!kCvtInValues) {
           pf[kb * 2 + (i >> 3)][i & 7] = (__bf16)pv[0];
           pf[kb * 2 + (i >> 3)][(i & 7) + 1] = (__bf16)pv[1];
         }
@@ -339,11 +343,19 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
         for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
     }
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+    for (int g = 0; g < 4; ++g) {
+      bf16x8 pg = pf[g];
+      if constexpr (kCvtInValues) {
+        // Keys 8 g .. 8 g + 7 of the lane's 32: element i of 32-key block kb
+        // is pe[16 kb + i], operand g holds block g / 2, elements 8 (g % 2) + t.
+#pragma unroll
+        for (int t = 0; t < 8; ++t) pg[t] = (__bf16)pe[8 * g + t];
+      }
 #pragma unroll
       for (int db = 0; db < TV::DB; ++db)
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            (g == 0 && NPRE) ? vpre[db] : rdv.col_op(vt, g, db), pf[g], oacc[db], 0, 0, 0);
+            (g == 0 && NPRE) ? vpre[db] : rdv.col_op(vt, g, db), pg, oacc[db], 0, 0, 0);
+    }
     if constexpr (DROPOUT) {
       dropout_row_words((uint32_t)(my_q + offset), (uint32_t)(j + 1), (uint32_t)bh, drop, hi, mw);
       // Eight transposed V reads in flight, then two more per product.
@@ -388,7 +400,13 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
       // The probabilities must be complete here, inside the region shared with
       // the score products: without this use the compiler sinks the
       // exponentials below the rescale branch, out of reach of the interleave.
-      asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(pf[2]), "v"(pf[3]));
+      if constexpr (kCvtInValues) {
+#pragma unroll
+        for (int i = 0; i < 32; i += 4)
+          asm volatile("" ::"v"(pe[i]), "v"(pe[i + 1]), "v"(pe[i + 2]), "v"(pe[i + 3]));
+      } else {
+        asm volatile("" ::"v"(pf[0]), "v"(pf[1]), "v"(pf[2]), "v"(pf[3]));
+      }
     } else {
       alpha = softmax(s_cur, pf);   // the wave's last tile: nothing to overlap
     }
