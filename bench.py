@@ -678,6 +678,35 @@ def time_sweep(stream, steps: int, warmup: int):
 
 # ---------------------------------------------------------------- counter passes
 
+def time_library_gemm(stream, n: int = 8192) -> dict:
+    """The vendor BLAS library's bf16 GEMM (torch.matmul, n x n x n) timed the
+    same way in the same process: the matrix rate a plain library contraction
+    reaches on this chip at the clock it sustains, beside the attention
+    kernels' fractions of the published peak.  Context only: no attention
+    arithmetic runs here."""
+    import torch
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(7)
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+
+    def mm():
+        torch.matmul(a, b, out=c)
+
+    warm_for(mm, 1.0)
+    per = per_launch_ms(mm, stream, 5, batch=20)
+    ms = statistics.median(per)
+    tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    out = {"what": "torch.matmul bf16 %d x %d x %d (ROCm BLAS library), context for the "
+                   "attention kernels' fractions of peak" % (n, n, n),
+           "ms": round(ms, 5), "tflops": round(tf, 1),
+           "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    del a, b, c
+    torch.cuda.empty_cache()
+    return out
+
+
 def counter_pass(w, launches: int = 3):
     """For rocprofv3 --pmc runs: one plain device copy of COPY_BYTES (the
     calibration dispatch), then ``launches`` dispatches of each measured path
@@ -851,6 +880,8 @@ def main():
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-dropout", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-gemm", action="store_true",
+                    help="skip the library GEMM context figure")
     ap.add_argument("--no-device-probe", action="store_true",
                     help="no helper programs (driver/compiler versions, clock sampler)")
     ap.add_argument("--counter-pass", action="store_true",
@@ -968,6 +999,9 @@ def main():
         out["general_shapes"] = time_general(stream, max(5, args.steps // 2), max(2, args.warmup // 2))
     if not args.no_sweep:
         out["seq_sweep"] = time_sweep(stream, min(args.steps, 20), max(2, args.warmup // 10))
+    if not args.no_gemm:
+        out["library_gemm"] = time_library_gemm(stream)
+        out["library_gemm"]["forward_over_gemm"] = round(achieved / out["library_gemm"]["tflops"], 4)
     if not args.no_cpu_baseline:
         if configs is not None:
             add_config_oracle(configs)
