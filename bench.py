@@ -125,9 +125,11 @@ def roofline_hbm(gbs: float, traffic=None) -> dict:
 
 
 def event_ms(fn, stream, calls: int, warmup: int) -> float:
-    """Average ms of ``fn`` over ``calls`` calls after ``warmup`` untimed ones,
-    from HIP events recorded on the launch stream."""
+    """Average ms of ``fn`` over ``calls`` calls after about 0.25 s of untimed
+    back-to-back calls (the clock this load holds) and ``warmup`` more, from
+    HIP events recorded on the launch stream."""
     import torch
+    warm_for(fn, 0.25)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -429,6 +431,7 @@ def time_backward(w, q, k, v, o, lse, stream, steps: int, warmup: int):
         ta.attn_bwd(q, k, v, o, lse, g, w.scale, w.causal, workspace=ws, grads=grads,
                     stream=stream.cuda_stream)
 
+    warm_for(bstep, 0.25)   # the gradient's host-side set-up left the GPU idle
     for _ in range(warmup):
         bstep()
     torch.cuda.synchronize()
@@ -930,6 +933,11 @@ def main():
 
     configs = None if args.no_configs else time_configs(stream)
 
+    # The other legs' host-side set-up leaves the GPU idle for a while and its
+    # clock drops; run the headline back to back for about 0.5 s (untimed)
+    # before the W warm-up steps, so the timed steps see the clock this load
+    # holds whatever W is.
+    warm_for(step, 0.5)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
