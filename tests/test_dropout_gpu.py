@@ -220,6 +220,24 @@ GENERAL_CASES = {  # name: (B, H, Nq, Nk, d, dv, offset, causal)
 }
 
 
+def _random_general(n: int, seed: int):
+    """Seeded random shapes beside the named ones (the same set on every run);
+    at least two keys, so the gradients do not vanish identically."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for i in range(n):
+        nk = int(rng.integers(2, 1101))
+        causal = bool(rng.integers(0, 2))
+        out["random_%02d" % i] = (int(rng.integers(1, 3)), int(rng.integers(1, 4)),
+                                  int(rng.integers(1, 401)), nk, int(rng.choice([64, 128])),
+                                  int(rng.choice([64, 128])),
+                                  int(rng.integers(0, nk + 32)) if causal else 0, causal)
+    return out
+
+
+GENERAL_CASES.update(_random_general(6, 9909))
+
+
 def _general_inputs(B, H, Nq, Nk, d, dv, seed):
     g = torch.Generator().manual_seed(seed)
     q = torch.randn((B, H, Nq, d), generator=g)

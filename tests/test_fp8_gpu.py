@@ -279,6 +279,24 @@ FP8_GENERAL = {  # name: (B, H, Nq, Nk, d, dv, offset, causal, mult)
 }
 
 
+def _random_general(n: int, seed: int):
+    """Seeded random shapes beside the named ones (the same set on every run)."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for i in range(n):
+        nk = int(rng.integers(1, 1101))
+        causal = bool(rng.integers(0, 2))
+        out["random_%02d" % i] = (int(rng.integers(1, 3)), int(rng.integers(1, 4)),
+                                  int(rng.integers(1, 401)), nk, int(rng.choice([64, 128])),
+                                  int(rng.choice([64, 128])),
+                                  int(rng.integers(0, nk + 32)) if causal else 0, causal,
+                                  float(rng.choice([1.0, 4.0])))
+    return out
+
+
+FP8_GENERAL.update(_random_general(6, 8808))
+
+
 @pytest.mark.parametrize("name", sorted(FP8_GENERAL))
 def test_fp8_general_shapes(name):
     B, H, Nq, Nk, d, dv, off, causal, mult = FP8_GENERAL[name]
