@@ -281,8 +281,9 @@ void attn_fwd_kernel(const void* __restrict__ Qv, const void* __restrict__ Kv,
                                      : __builtin_amdgcn_exp2f((POS_SCALE ? m * scale_log2 : m) - cref);
     m = m_new;
     // p = 2^(c s - c m'); positive scale: one fused multiply-add per element.
-    // The row maximum itself gets p = 1 exactly, so the dominant weight carries
-    // no bf16 rounding into the value product.
+    // For the row maximum itself the argument is only the rounding residual of
+    // c m (|r| <= 2^-24 |c m|), so its p rounds to exactly 1 in bf16: the
+    // dominant weight carries no bf16 rounding into the value product.
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
